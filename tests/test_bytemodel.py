@@ -1,0 +1,64 @@
+"""Byte/FLOP model pinned to the numbers the asymmetric-KV page prints."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from mixed_precision_paged_amd import bytemodel
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "asym_byte_model.json")))
+
+
+def test_bytes_per_pair_and_capacity():
+    g = GOLD["bytes_per_pair"]
+    for k in ("K16/V16", "K16/V8", "K8/V8"):
+        assert bytemodel.BYTES_PER_PAIR[k] == g[k]
+        cap = bytemodel.BYTES_PER_PAIR["K16/V16"] / bytemodel.BYTES_PER_PAIR[k]
+        assert round(cap, 2) == g["capacity_vs_K16V16"][k]
+
+
+def test_worked_bandwidth_example():
+    w = GOLD["worked_example"]
+    per_tok = bytemodel.kv_bytes_per_token(w["layers"], w["kv_heads"], w["head_dim"], "K16/V16")
+    assert per_tok == w["bytes_per_token_K16V16_KiB"] * 1024
+    for layout in ("K16/V16", "K16/V8", "K8/V8"):
+        payload = bytemodel.kv_payload_bytes(w["tokens"], w["layers"], w["kv_heads"], w["head_dim"], layout)
+        assert payload == w["payload_GiB"][layout] * 2 ** 30
+        assert round(bytemodel.reread_gbps(payload, 0.010), 1) == w["reread_10ms_GBps"][layout]
+        assert round(bytemodel.reread_gbps(payload, 1.0), 2) == w["reload_1s_GBps"][layout]
+
+
+def test_token_slots_per_layer():
+    s = GOLD["token_slots"]
+    for layout in ("K16/V16", "K16/V8"):
+        n = bytemodel.token_slots(s["pool_bytes"], s["layers"], s["kv_heads"], s["head_dim"], layout)
+        assert n == s[layout]
+        assert n * bytemodel.kv_bytes_per_token(s["layers"], s["kv_heads"], s["head_dim"], layout) == s["pool_bytes"]
+
+
+def test_workspace_payload_size():
+    w = GOLD["workspace"]
+    _, written = bytemodel.gather_bytes(w["max_pages"], 8, 128)
+    assert written == w["payload_MiB"] * 2 ** 20
+    assert w["max_pages"] * 4 == w["indices_KiB"] * 1024
+
+
+def test_decode_bytes_compact_batch():
+    lens = [8192] * 32
+    fid = np.ones((32, 512), np.uint8)
+    b = bytemodel.decode_bytes(lens, fid, 32, 8, 128, out_bytes=2, flags_read=False)
+    assert b == 805306368 + 524288 + 65536 + 262144 + 262144
+
+
+def test_decode_bytes_counts_target_values_twice_and_partial_pages():
+    fid = np.array([[0, 1, 0]], np.uint8)
+    b = bytemodel.decode_bytes([40], fid, 2, 1, 4, out_bytes=4, lse=True)
+    # tokens per page 16, 16, 8; K 2 B; V 2/1/2 B; one scale; ids + flags
+    kv = 40 * 4 * 2 + (16 * 2 + 16 * 1 + 8 * 2) * 4
+    assert b == kv + 4 + 3 * 5 + 2 * 4 * 2 + 2 * 4 * 4 + 2 * 4
+
+
+def test_prefill_flops():
+    assert bytemodel.prefill_flops([8192] * 32, 32, 128) == 32 * 2 * 128 * 32 * 8192 * 8193
+    assert bytemodel.prefill_flops([3], 1, 1, causal=False) == 4 * 9

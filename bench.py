@@ -1,0 +1,183 @@
+"""Benchmark: mixed-fidelity paged decode attention on one MI355X.
+
+Headline workload: compact decode, batch 32, context 8192, 32 query / 8 KV
+heads, head dim 128, 16-token pages, FP16 K + E4M3 V with per-page-head fp32
+scales, seeded synthetic N(0,1) data, page table a random permutation of a
+17,408-page pool.  One step = one ekv_decode_attention call (split-K kernel +
+merge kernel) over the whole batch, with the per-page fidelity flags read.
+
+Prints ONE JSON line: decode HBM GB/s (algorithmic bytes / step time), with
+tokens/s, a roofline object for the decode call and the CPU oracle timed on
+the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode attention HBM GB/s (% of peak) + tokens/s, B=32 ctx 8K K16/V8"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=2,
+                    help="pool copies rotated across steps so no step re-reads cached pages")
+    ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--no-flags", action="store_true", help="single-pool path (no per-page flag reads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the decode hot path on a single MI355X "
+              "(sequences and KV heads shard across GPUs with no exchange; not built here).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixed_precision_paged_amd import bytemodel, ekv, synth
+
+    t0 = time.time()
+    case = synth.compact_decode_case(seed=2)
+    gen_s = time.time() - t0
+    B, Hq, Hkv, D = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    copies = []
+    for _ in range(max(1, args.copies)):
+        copies.append(dict(k=dev(case.k_compact), v=dev(case.v_compact), s=dev(case.v_scale)))
+    q = dev(case.q)
+    pt = dev(case.page_table)
+    fl = None if args.no_flags else dev(case.fidelity)
+    lens = dev(case.seq_lens)
+    out = torch.empty((B, Hq, D), dtype=torch.float16, device="cuda")
+    scratch_bytes = ekv.ekv_decode_scratch_bytes(B, Hq, Hkv, D, case.max_seq_len, args.pages_per_split)
+    scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device="cuda")
+    kvs = [ekv.paged_kv(Hkv, D, k_compact=c["k"], v_compact=c["v"], v_scale=c["s"]) for c in copies]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ekv.ekv_decode_attention(kvs[i % len(kvs)], q, pt, fl, lens, case.max_seq_len, case.sm_scale,
+                                 out, None, scratch, pages_per_split=args.pages_per_split,
+                                 stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events on the launch stream around each decode call
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    algo_bytes = bytemodel.decode_bytes(case.seq_lens, case.fidelity, Hq, Hkv, D, out_bytes=2,
+                                        lse=False, flags_read=fl is not None)
+    ms_per_step = wall * 1e3 / args.steps
+    value = algo_bytes / (ms_per_step * 1e-3) / 1e9
+    kernel_ms = float(per_call_ms.mean())
+    achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, algo_bytes, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "compact paged decode: batch 32, context 8192, 32 q / 8 KV heads, head dim 128, "
+                        "page 16, FP16 K + E4M3 V + fp32 page-head scales, 17,408-page pool (seed 2)",
+            "batch": B, "context": int(case.seq_lens[0]), "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_dim": D, "page_size": 16, "fidelity_flags_read": fl is not None,
+            "pages_per_split": args.pages_per_split or ekv.ekv_decode_pages_per_split(B, Hkv, case.max_seq_len),
+            "pool_copies_rotated": len(kvs), "out_dtype": "f16",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": int(algo_bytes),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "ekv_decode_attention (decode_splitk_kernel + decode_merge_kernel)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_call_us": round(kernel_ms * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+        "input_generation_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(case, algo_bytes, min_seconds):
+    """The float64 oracle on the host cores over the same batch, repeated to >= min_seconds."""
+    import oracle  # CPU baseline leg only
+
+    try:
+        import threadpoolctl
+        blas = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:  # threadpoolctl absent: numpy's default
+        blas = os.cpu_count() or 1
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode_attention(case.q, case.k_target, case.v_target, case.k_compact, case.v_compact,
+                                case.v_scale, case.page_table, case.fidelity, case.seq_lens,
+                                case.sm_scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {
+        "value": round(algo_bytes * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(blas),
+        "host_cpu_count": os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"the whole batch (32 sequences x 8192 tokens) decoded {reps}x by the float64 "
+                  f"oracle in {el:.1f} s",
+        "tokens_per_s": round(case.batch * reps / el, 3),
+    }
+
+
+if __name__ == "__main__":
+    main()

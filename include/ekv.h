@@ -1,0 +1,220 @@
+/*
+ * ekv.h — C ABI of libekv.so: attention over a mixed-fidelity paged KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page titles as published):
+ *   [ekv]  "Does Execution Require Target KV Fidelity? A Mixed-Fidelity KV
+ *          Runtime for LLM Serving" (ElasticKV).
+ *   [asym] "Memory-Traffic Saturation in Autoregressive Transformer Decode"
+ *          (asymmetric K16/V8 KV cache).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, densely packed in the layouts stated below.  The library never
+ *     allocates, frees or synchronizes; every launch is asynchronous on
+ *     `stream` (a hipStream_t; NULL = the default stream).
+ *   - Page layout (NHD): a page holds EKV_PAGE_SIZE tokens, each token all
+ *     KV heads, each head `head_dim` contiguous elements:
+ *     pool[page][slot][kv_head][d].  [asym] "What changes in vLLM's prefill
+ *     routing?": NHD layout, page size 16, FP16 keys, FP8 E4M3 values.
+ *   - FP8 values use the OCP E4M3FN encoding (bias 7, max 448, NaN 0x7F/0xFF).
+ *   - Grouped-query attention: query head h reads KV head
+ *     h / (num_q_heads / num_kv_heads).
+ *   - Supported shapes: head_dim 64 or 128; num_q_heads / num_kv_heads in
+ *     {1, 2, 4, 8}; page_size 16.  Others return EKV_ERR_UNSUPPORTED.
+ *   - Errors: arguments are checked on the host before any launch; a non-OK
+ *     status means nothing was launched.  ekv_last_error() then returns a
+ *     thread-local message.  Launch failures return EKV_ERR_HIP.  No C++
+ *     exception crosses the ABI.
+ *   - Device-resident contents (page ids, flags, lengths, offsets) cannot be
+ *     checked on the host.  Kernels bound-check them before any memory
+ *     access: an out-of-range page id, an unknown fidelity flag, or prompt
+ *     offsets outside the buffers never cause an out-of-bounds access; the
+ *     affected output rows are written as NaN instead.
+ *   - Output slices: each call writes only its own rows; pass an offset
+ *     pointer to write a slice of a larger batch tensor ([asym] figure
+ *     "Fresh prefill gets a fast path inside a mixed batch": each path writes
+ *     its own output slice in the original request order).
+ */
+#ifndef EKV_H_
+#define EKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EKV_ABI_VERSION 1
+#define EKV_PAGE_SIZE 16
+#define EKV_FIDELITY_TARGET 0   /* FP16 K + FP16 V                        */
+#define EKV_FIDELITY_COMPACT 1  /* FP16 K + E4M3 V + fp32 scale/page/head  */
+#define EKV_MAX_PREFILL_TOKENS 8192 /* [asym] route rule: prompts of at most 8,192 tokens */
+
+typedef enum {
+  EKV_OK = 0,
+  EKV_ERR_INVALID_ARG = 1,         /* null pointer, bad size or stride      */
+  EKV_ERR_UNSUPPORTED = 2,         /* shape outside the supported set       */
+  EKV_ERR_WORKSPACE_TOO_SMALL = 3, /* gather larger than the workspace      */
+  EKV_ERR_NOT_ELIGIBLE = 4,        /* prompt outside the prefill route rule */
+  EKV_ERR_HIP = 5                  /* a HIP launch failed                   */
+} ekv_status;
+
+typedef enum { EKV_F16 = 0, EKV_F32 = 1 } ekv_dtype;
+
+/*
+ * The paged KV of one attention layer: two physical pools.
+ * [ekv] section 3.2 and appendix B.3: a TARGET page and a compact page share
+ * one attention output interface; a per-page mode selects the load path.
+ * [asym] "What changes in vLLM's prefill routing?": compact pages keep FP16
+ * keys and store values as E4M3 with value scales.
+ *
+ *   k_target, v_target : fp16 [n_target_pages][16][num_kv_heads][head_dim]
+ *   k_compact          : fp16 [n_compact_pages][16][num_kv_heads][head_dim]
+ *   v_compact          : u8 E4M3FN [n_compact_pages][16][num_kv_heads][head_dim]
+ *   v_scale            : fp32 [n_compact_pages][num_kv_heads]; the value of a
+ *                        compact element is e4m3(byte) * v_scale[page][head]
+ * A pool that is not used may be NULL with its page count 0.
+ */
+typedef struct {
+  const void* k_target;
+  const void* v_target;
+  int32_t n_target_pages;
+  const void* k_compact;
+  const uint8_t* v_compact;
+  const float* v_scale;
+  int32_t n_compact_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size; /* must be EKV_PAGE_SIZE */
+} ekv_paged_kv;
+
+/* Version of this ABI (EKV_ABI_VERSION). */
+int32_t ekv_abi_version(void);
+
+/* Static description of a status code. */
+const char* ekv_status_string(ekv_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* ekv_last_error(void);
+
+/*
+ * Decode split plan: how many pages one split of a sequence covers when
+ * `pages_per_split` is 0 (automatic).  Pure host function.
+ */
+int32_t ekv_decode_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
+
+/*
+ * Scratch bytes ekv_decode_attention needs for these sizes (split-K partial
+ * results).  `pages_per_split` 0 = the automatic plan.  Pure host function.
+ */
+size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_seq_len, int32_t pages_per_split);
+
+/*
+ * GQA decode attention: one query token per sequence over its paged KV, in
+ * one launch for any mix of TARGET and compact pages.
+ * [asym] "What changes in vLLM's prefill routing?": decode reads persistent
+ * FP16 keys and FP8 values, and value scales apply in attention.
+ * [ekv] section 3.2: TARGET and compact pages execute in one batch and share
+ * one output interface; compact values are expanded in registers, never
+ * materialized as TARGET.
+ *
+ *   q          fp16 [batch][num_q_heads][head_dim]
+ *   page_table int32 [batch][pt_stride]: physical page of logical page j of
+ *              sequence b (token t lives in page t/16, slot t%16); ids index
+ *              the pool that the page's flag selects.
+ *   fidelity   u8 [batch][pt_stride]: EKV_FIDELITY_TARGET or _COMPACT.  May
+ *              be NULL when exactly one pool is given: every page then uses
+ *              that pool.
+ *   seq_lens   int32 [batch]: tokens of each sequence, including the token
+ *              being decoded (its K/V is already in the cache); the query
+ *              attends to tokens [0, len).  Values are clamped to
+ *              [0, max_seq_len]; len 0 gives out = 0 and lse = -inf.
+ *   max_seq_len  host upper bound of seq_lens (sizes the launch);
+ *              pt_stride must be >= ceil(max_seq_len / 16).
+ *   sm_scale   softmax scale (typically 1/sqrt(head_dim)).
+ *   out        [batch][num_q_heads][head_dim] in `out_dtype`.  In EKV_F16 the
+ *              value is the round-to-nearest-even of the EKV_F32 result.
+ *   lse        optional fp32 [batch][num_q_heads]: natural-log normalizer
+ *              max_t s_t + ln sum_t exp(s_t - max_t s_t).
+ *   pages_per_split  split-K granularity (0 = automatic; else 1..4096).
+ *   scratch    device buffer of at least ekv_decode_scratch_bytes(...) bytes
+ *              (same arguments), 256-byte aligned; contents are overwritten.
+ * Sequences that reference an out-of-range page id or an unknown flag get
+ * NaN outputs and NaN lse.
+ */
+ekv_status ekv_decode_attention(const ekv_paged_kv* kv, const void* q, int32_t batch,
+                                int32_t num_q_heads, const int32_t* page_table, int32_t pt_stride,
+                                const uint8_t* fidelity, const int32_t* seq_lens,
+                                int32_t max_seq_len, float sm_scale, void* out, ekv_dtype out_dtype,
+                                float* lse, int32_t pages_per_split, void* scratch,
+                                size_t scratch_bytes, void* stream);
+
+/*
+ * Compact-prefill gather: copy the listed compact pages into a bounded FP16
+ * workspace.  [asym] "What changes in vLLM's prefill routing?" (figure "Fresh
+ * prefill gets a fast path inside a mixed batch"): stored K16/V8 pages are
+ * gathered into one shared FP16 payload of at most 4,096 pages and V8 is cast
+ * to FP16.
+ *
+ *   page_ids   int32 [n_pages], indices into the compact pool.
+ *   ws_k, ws_v fp16 [ws_capacity_pages][16][num_kv_heads][head_dim]; page i of
+ *              the workspace receives pool page page_ids[i], so the workspace
+ *              is token-major [n_pages*16][num_kv_heads][head_dim].
+ *   apply_scale 0: ws_v = fp16(e4m3(byte))            (exact cast)
+ *               1: ws_v = fp16(fp32(e4m3(byte)) * fp32(scale))  (one fp32
+ *                  multiply, round-to-nearest-even, then one fp16 rounding,
+ *                  round-to-nearest-even)
+ *   Keys are copied bit for bit.  E4M3 NaN codes become FP16 NaN.
+ * n_pages > ws_capacity_pages returns EKV_ERR_WORKSPACE_TOO_SMALL.  An
+ * out-of-range page id fills that workspace page with NaN.
+ */
+ekv_status ekv_gather_compact_pages(const ekv_paged_kv* kv, const int32_t* page_ids,
+                                    int32_t n_pages, int32_t apply_scale, void* ws_k, void* ws_v,
+                                    int32_t ws_capacity_pages, void* stream);
+
+/*
+ * Causal FP16 prefill attention of fresh prompts over contiguous K/V rows
+ * (the gather workspace).  [asym] "What changes in vLLM's prefill routing?":
+ * whole fresh prompts with no cached prefix, FP16 Q/K/V, causal attention
+ * without sliding windows, attention sinks or soft caps.
+ *
+ *   q            fp16 [q_rows][num_q_heads][head_dim]; prompt p owns rows
+ *                [cu_seqlens_q[p], cu_seqlens_q[p+1]).
+ *   k, v         fp16 [kv_rows][num_kv_heads][head_dim]; prompt p's keys are
+ *                rows [kv_start[p], kv_start[p] + len_p), len_p = its query
+ *                count (q_len == kv_len).
+ *   cu_seqlens_q int32 [n_prompts + 1], kv_start int32 [n_prompts] (device).
+ *   max_len      host bound of every len_p; > EKV_MAX_PREFILL_TOKENS returns
+ *                EKV_ERR_NOT_ELIGIBLE (the caller chunks or falls back).
+ *   causal       1: query i sees keys 0..i of its prompt; 0: all len_p keys.
+ *   out          [q_rows][num_q_heads][head_dim] in out_dtype (F16 = RNE of
+ *                the F32 result); rows outside every prompt are not written.
+ *   lse          optional fp32 [q_rows][num_q_heads], natural log.
+ * A prompt whose offsets leave the buffers or exceed max_len is not read;
+ * its in-bounds output rows are written as NaN.
+ */
+ekv_status ekv_prefill_attention(const void* q, int32_t q_rows, const void* k, const void* v,
+                                 int32_t kv_rows, const int32_t* cu_seqlens_q,
+                                 const int32_t* kv_start, int32_t n_prompts, int32_t max_len,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t causal, float sm_scale, void* out, ekv_dtype out_dtype,
+                                 float* lse, void* stream);
+
+/*
+ * Diagnostic for the device E4M3 decoding used by the kernels: converts n
+ * codes to fp16.  method 0 = the decode kernel's path (codes packed four per
+ * 32-bit word, scale 1), 2 = the same path with scale 2^-7 (so out =
+ * fp16(e4m3 * 2^-7)), 1 = the gather kernel's path.  codes u8 [n], out fp16
+ * [n] (device).  Other methods return EKV_ERR_INVALID_ARG.
+ */
+ekv_status ekv_e4m3_to_f16(const uint8_t* codes, int32_t n, void* out, int32_t method,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EKV_H_ */

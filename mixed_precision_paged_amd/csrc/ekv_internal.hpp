@@ -1,0 +1,75 @@
+// Host-side declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ekv {
+
+struct DecodeParams {
+  const uint16_t* k_target;
+  const uint16_t* v_target;
+  int32_t n_target;
+  const uint16_t* k_compact;
+  const uint8_t* v_compact;
+  const float* v_scale;
+  int32_t n_compact;
+  const uint16_t* q;
+  const int32_t* page_table;
+  int32_t pt_stride;
+  const uint8_t* fidelity;  // NULL: every page has kind `uniform_kind`
+  int32_t uniform_kind;
+  const int32_t* seq_lens;
+  int32_t batch, num_q_heads, num_kv_heads, head_dim, max_seq_len;
+  int32_t pages_per_split, n_splits;
+  float scale_log2;  // sm_scale * log2(e)
+  float* part_acc;   // [batch][Hkv][n_splits][G][D]
+  float* part_ml;    // [batch][Hkv][n_splits][G][2]  (max in log2 units, sum)
+  void* out;
+  int32_t out_f32;
+  float* lse;
+};
+
+struct GatherParams {
+  const uint16_t* k_compact;
+  const uint8_t* v_compact;
+  const float* v_scale;
+  int32_t n_pool;
+  const int32_t* page_ids;
+  int32_t n_pages;
+  int32_t num_kv_heads, head_dim;
+  int32_t apply_scale;
+  uint16_t* ws_k;
+  uint16_t* ws_v;
+};
+
+struct PrefillParams {
+  const uint16_t* q;
+  int32_t q_rows;
+  const uint16_t* k;
+  const uint16_t* v;
+  int32_t kv_rows;
+  const int32_t* cu_seqlens_q;
+  const int32_t* kv_start;
+  int32_t n_prompts, max_len;
+  int32_t num_q_heads, num_kv_heads, head_dim;
+  int32_t causal;
+  float scale_log2;
+  void* out;
+  int32_t out_f32;
+  float* lse;
+};
+
+// Split plan shared by the scratch query and the launch.
+int32_t decode_auto_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages);
+size_t decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t n_splits);
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_e4m3_to_f16(const uint8_t* codes, int32_t n, uint16_t* out, int32_t method,
+                              hipStream_t stream);
+
+}  // namespace ekv

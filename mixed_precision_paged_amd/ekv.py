@@ -1,0 +1,189 @@
+"""Python binding of libekv.so (C ABI in include/ekv.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, statuses become exceptions.  Every step of the
+computation runs in the HIP kernels of libekv.so; there is no fallback.
+Importing this module raises ImportError if the library has not been built
+(``python -m mixed_precision_paged_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libekv.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mixed_precision_paged_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+PAGE_SIZE = 16
+FIDELITY_TARGET = 0
+FIDELITY_COMPACT = 1
+MAX_PREFILL_TOKENS = 8192
+
+EKV_OK = 0
+EKV_ERR_INVALID_ARG = 1
+EKV_ERR_UNSUPPORTED = 2
+EKV_ERR_WORKSPACE_TOO_SMALL = 3
+EKV_ERR_NOT_ELIGIBLE = 4
+EKV_ERR_HIP = 5
+EKV_F16 = 0
+EKV_F32 = 1
+
+EXPORTED = (
+    "ekv_abi_version", "ekv_status_string", "ekv_last_error", "ekv_decode_pages_per_split",
+    "ekv_decode_scratch_bytes", "ekv_decode_attention", "ekv_gather_compact_pages",
+    "ekv_prefill_attention", "ekv_e4m3_to_f16",
+)
+
+
+class PagedKV(ctypes.Structure):
+    _fields_ = [
+        ("k_target", ctypes.c_void_p), ("v_target", ctypes.c_void_p), ("n_target_pages", ctypes.c_int32),
+        ("k_compact", ctypes.c_void_p), ("v_compact", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("n_compact_pages", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+    ]
+
+
+_i32, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_lib.ekv_abi_version.restype = _i32
+_lib.ekv_status_string.restype = ctypes.c_char_p
+_lib.ekv_status_string.argtypes = [ctypes.c_int]
+_lib.ekv_last_error.restype = ctypes.c_char_p
+_lib.ekv_decode_pages_per_split.restype = _i32
+_lib.ekv_decode_pages_per_split.argtypes = [_i32, _i32, _i32]
+_lib.ekv_decode_scratch_bytes.restype = _sz
+_lib.ekv_decode_scratch_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+_lib.ekv_decode_attention.restype = ctypes.c_int
+_lib.ekv_decode_attention.argtypes = [
+    ctypes.POINTER(PagedKV), _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _f32, _vp, ctypes.c_int,
+    _vp, _i32, _vp, _sz, _vp]
+_lib.ekv_gather_compact_pages.restype = ctypes.c_int
+_lib.ekv_gather_compact_pages.argtypes = [ctypes.POINTER(PagedKV), _vp, _i32, _i32, _vp, _vp, _i32, _vp]
+_lib.ekv_prefill_attention.restype = ctypes.c_int
+_lib.ekv_prefill_attention.argtypes = [
+    _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, ctypes.c_int,
+    _vp, _vp]
+_lib.ekv_e4m3_to_f16.restype = ctypes.c_int
+_lib.ekv_e4m3_to_f16.argtypes = [_vp, _i32, _vp, _i32, _vp]
+
+
+class EkvError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{ekv_status_string(status)} ({status}): {detail}")
+
+
+def ekv_abi_version() -> int:
+    return int(_lib.ekv_abi_version())
+
+
+def ekv_status_string(status: int) -> str:
+    return _lib.ekv_status_string(int(status)).decode()
+
+
+def ekv_last_error() -> str:
+    return _lib.ekv_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != EKV_OK:
+        raise EkvError(status, ekv_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libekv must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return EKV_F16
+    if t.dtype == torch.float32:
+        return EKV_F32
+    raise TypeError(f"output dtype {t.dtype} is not float16/float32")
+
+
+def paged_kv(num_kv_heads: int, head_dim: int, k_target=None, v_target=None, k_compact=None,
+             v_compact=None, v_scale=None) -> PagedKV:
+    """Descriptor of one layer's page pools (tensors stay owned by the caller)."""
+    n_t = int(k_target.shape[0]) if k_target is not None else 0
+    n_c = int(k_compact.shape[0]) if k_compact is not None else 0
+    for t, dt in ((k_target, torch.float16), (v_target, torch.float16), (k_compact, torch.float16),
+                  (v_compact, torch.uint8), (v_scale, torch.float32)):
+        if t is not None and t.dtype != dt:
+            raise TypeError(f"pool tensor has dtype {t.dtype}, expected {dt}")
+    return PagedKV(_ptr(k_target), _ptr(v_target), n_t, _ptr(k_compact), _ptr(v_compact),
+                   _ptr(v_scale), n_c, num_kv_heads, head_dim, PAGE_SIZE)
+
+
+def ekv_decode_pages_per_split(batch: int, num_kv_heads: int, max_seq_len: int) -> int:
+    return int(_lib.ekv_decode_pages_per_split(batch, num_kv_heads, max_seq_len))
+
+
+def ekv_decode_scratch_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                             max_seq_len: int, pages_per_split: int = 0) -> int:
+    return int(_lib.ekv_decode_scratch_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                             max_seq_len, pages_per_split))
+
+
+def ekv_decode_attention(kv: PagedKV, q: torch.Tensor, page_table: torch.Tensor,
+                         fidelity: Optional[torch.Tensor], seq_lens: torch.Tensor, max_seq_len: int,
+                         sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                         scratch: Optional[torch.Tensor] = None, pages_per_split: int = 0,
+                         stream=None) -> None:
+    """GQA decode over paged TARGET/compact KV (see ekv.h).  Writes ``out`` (and ``lse``)."""
+    batch, hq, _ = q.shape
+    if scratch is None:
+        need = ekv_decode_scratch_bytes(batch, hq, kv.num_kv_heads, kv.head_dim, max_seq_len,
+                                        pages_per_split)
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.ekv_decode_attention(
+        ctypes.byref(kv), _ptr(q), batch, hq, _ptr(page_table), int(page_table.shape[1]),
+        _ptr(fidelity), _ptr(seq_lens), int(max_seq_len), float(sm_scale), _ptr(out),
+        _dtype_code(out), _ptr(lse), int(pages_per_split), _ptr(scratch),
+        scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def ekv_gather_compact_pages(kv: PagedKV, page_ids: torch.Tensor, apply_scale: bool,
+                             ws_k: torch.Tensor, ws_v: torch.Tensor, n_pages: Optional[int] = None,
+                             stream=None) -> None:
+    """Gather compact pages into the FP16 workspace (see ekv.h)."""
+    n = int(page_ids.shape[0]) if n_pages is None else int(n_pages)
+    _check(_lib.ekv_gather_compact_pages(
+        ctypes.byref(kv), _ptr(page_ids), n, 1 if apply_scale else 0, _ptr(ws_k), _ptr(ws_v),
+        int(ws_k.shape[0]), _stream(stream)))
+
+
+def ekv_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          cu_seqlens_q: torch.Tensor, kv_start: torch.Tensor, max_len: int,
+                          sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                          causal: bool = True, stream=None) -> None:
+    """Causal FP16 prefill over contiguous K/V rows (see ekv.h).
+
+    q: [T, Hq, D]; k, v: [R, Hkv, D] (or the workspace view [pages, 16, Hkv, D])."""
+    q_rows, hq, d = q.shape
+    hkv = int(k.shape[-2])
+    kv_rows = k.numel() // (hkv * d)
+    _check(_lib.ekv_prefill_attention(
+        _ptr(q), q_rows, _ptr(k), _ptr(v), kv_rows, _ptr(cu_seqlens_q), _ptr(kv_start),
+        int(kv_start.shape[0]), int(max_len), hq, hkv, d, 1 if causal else 0, float(sm_scale),
+        _ptr(out), _dtype_code(out), _ptr(lse), _stream(stream)))
+
+
+def ekv_e4m3_to_f16(codes: torch.Tensor, out: torch.Tensor, method: int, stream=None) -> None:
+    """Diagnostic: device E4M3 -> fp16 conversion (0 = decode path, 1 = gather path)."""
+    _check(_lib.ekv_e4m3_to_f16(_ptr(codes), int(codes.numel()), _ptr(out), int(method), _stream(stream)))

@@ -15,9 +15,11 @@ compact page, and one batch mixes both.
 
 Recipe (stated once, used everywhere):
   * values are N(0,1) drawn in float32 from numpy PCG64(seed), then rounded
-    to FP16 (round-to-nearest-even);
+    to FP16 (round-to-nearest-even); pools are drawn 256 pages at a time in
+    the order K_target, V_target, K_compact, V_compact, then the queries;
   * optional outliers: each V element independently (probability
-    ``outlier_frac``) is multiplied by ``outlier_mult`` before the FP16 cast;
+    ``outlier_frac``, drawn after the chunk's normals) is multiplied by
+    ``outlier_mult`` before the FP16 cast;
   * compact pages store K as FP16 and V as E4M3FN bytes with one fp32 scale
     per (page, KV head) = fp32(absmax over the page's *valid* tokens x D of
     the FP16 V) / 448; an all-zero page gets scale 1.0.  The E4M3 encoding is
@@ -52,9 +54,16 @@ def _rng(seed: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(seed))
 
 
+def _to_fp16(x32: np.ndarray) -> np.ndarray:
+    """float32 -> float16, round to nearest even (torch's multi-threaded CPU cast)."""
+    import torch
+
+    return torch.from_numpy(x32).to(torch.float16).numpy()
+
+
 def normal_fp16(rng: np.random.Generator, shape) -> np.ndarray:
     """N(0,1) drawn in float32, rounded to FP16."""
-    return rng.standard_normal(size=shape, dtype=np.float32).astype(np.float16)
+    return _to_fp16(rng.standard_normal(size=shape, dtype=np.float32))
 
 
 def _values_with_outliers(rng, shape, outlier_frac, outlier_mult) -> np.ndarray:
@@ -62,7 +71,19 @@ def _values_with_outliers(rng, shape, outlier_frac, outlier_mult) -> np.ndarray:
     if outlier_frac > 0.0:
         mask = rng.random(size=shape, dtype=np.float32) < np.float32(outlier_frac)
         v[mask] *= np.float32(outlier_mult)
-    return v.astype(np.float16)
+    return _to_fp16(v)
+
+
+_CHUNK_PAGES = 256  # pages generated per draw (bounds host temporaries)
+
+
+def _pool_fp16(rng, pages, H, D, outlier_frac, outlier_mult) -> np.ndarray:
+    """fp16 [pages, 16, H, D] pool drawn chunk by chunk (normals, then outlier draws, per chunk)."""
+    out = np.empty((pages, PAGE_SIZE, H, D), dtype=np.float16)
+    for lo in range(0, pages, _CHUNK_PAGES):
+        hi = min(pages, lo + _CHUNK_PAGES)
+        out[lo:hi] = _values_with_outliers(rng, (hi - lo, PAGE_SIZE, H, D), outlier_frac, outlier_mult)
+    return out
 
 
 def quantize_pages_e4m3(v16: np.ndarray, valid_slots: np.ndarray):
@@ -71,21 +92,22 @@ def quantize_pages_e4m3(v16: np.ndarray, valid_slots: np.ndarray):
     v16: float16 [P, 16, Hkv, D]; valid_slots: int [P] tokens a page holds.
     Slots at or past ``valid_slots`` are ignored for the scale and poisoned.
     """
-    import torch  # library cast for the E4M3 encoding
+    import torch  # library casts (E4M3 encoding, fp16 -> fp32)
 
     P, S, H, D = v16.shape
-    v32 = v16.astype(np.float32)
-    slot = np.arange(S)[None, :, None, None]
-    valid = slot < valid_slots[:, None, None, None]
-    absmax = np.where(valid, np.abs(v32), np.float32(0)).max(axis=(1, 3))  # [P, H]
-    scale = (absmax / np.float32(E4M3_MAX)).astype(np.float32)
-    scale = np.where(absmax > 0, scale, np.float32(1.0)).astype(np.float32)
-    scaled = np.clip(v32 / scale[:, None, :, None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
-    codes = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
-    codes[~np.broadcast_to(valid, codes.shape)] = E4M3_NAN_CODE
-    empty = valid_slots <= 0
-    scale[empty] = np.float32(np.nan)
-    return codes, scale
+    v32 = torch.from_numpy(v16).to(torch.float32)                       # exact
+    slot_max = v32.abs().amax(dim=3)                                     # [P, 16, H]
+    valid = torch.arange(S)[None, :] < torch.from_numpy(np.asarray(valid_slots))[:, None]  # [P, 16]
+    absmax = torch.where(valid[:, :, None], slot_max, torch.zeros(())).amax(dim=1)  # [P, H]
+    scale = absmax / np.float32(E4M3_MAX)                                # fp32 division
+    scale = torch.where(absmax > 0, scale, torch.ones(()))
+    scaled = (v32 / scale[:, None, :, None]).clamp_(-E4M3_MAX, E4M3_MAX)
+    codes = scaled.to(torch.float8_e4m3fn).view(torch.uint8)
+    del scaled, v32
+    codes[~valid] = int(E4M3_NAN_CODE)
+    scale = scale.numpy().astype(np.float32)
+    scale[np.asarray(valid_slots) <= 0] = np.float32(np.nan)
+    return codes.numpy(), scale
 
 
 def _poison_fp16(pool: np.ndarray, valid_slots: np.ndarray) -> None:
@@ -190,15 +212,18 @@ def make_paged_case(
     valid_t[perm_t] = slot_count[is_target]
 
     H, D = num_kv_heads, head_dim
-    k_target = normal_fp16(rng, (P_T, PAGE_SIZE, H, D))
-    v_target = _values_with_outliers(rng, (P_T, PAGE_SIZE, H, D), outlier_frac, outlier_mult)
+    k_target = _pool_fp16(rng, P_T, H, D, 0.0, outlier_mult)
+    v_target = _pool_fp16(rng, P_T, H, D, outlier_frac, outlier_mult)
     _poison_fp16(k_target, valid_t)
     _poison_fp16(v_target, valid_t)
 
-    k_compact = normal_fp16(rng, (P_C, PAGE_SIZE, H, D))
-    v16 = _values_with_outliers(rng, (P_C, PAGE_SIZE, H, D), outlier_frac, outlier_mult)
-    v_compact, v_scale = quantize_pages_e4m3(v16, valid_c)
-    del v16
+    k_compact = _pool_fp16(rng, P_C, H, D, 0.0, outlier_mult)
+    v_compact = np.empty((P_C, PAGE_SIZE, H, D), dtype=np.uint8)
+    v_scale = np.empty((P_C, H), dtype=np.float32)
+    for lo in range(0, P_C, _CHUNK_PAGES):
+        hi = min(P_C, lo + _CHUNK_PAGES)
+        v16 = _values_with_outliers(rng, (hi - lo, PAGE_SIZE, H, D), outlier_frac, outlier_mult)
+        v_compact[lo:hi], v_scale[lo:hi] = quantize_pages_e4m3(v16, valid_c[lo:hi])
     _poison_fp16(k_compact, valid_c)
 
     rows = B if query_rows is None else query_rows

@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/ekv.h declares, and host-side validation returns the documented
+status before any launch (all cases below are rejected on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ekv.h")
+
+ekv = pytest.importorskip("mixed_precision_paged_amd.ekv", reason="libekv.so not built")
+
+FAKE = 0x10000  # aligned non-null address; never dereferenced: every call below fails validation
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(ekv_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(ekv._lib, n), n
+    assert sorted(ekv.EXPORTED) == names
+
+
+def test_version_and_status_strings():
+    assert ekv.ekv_abi_version() == 1
+    assert ekv.ekv_status_string(ekv.EKV_OK) == "ok"
+    assert "workspace" in ekv.ekv_status_string(ekv.EKV_ERR_WORKSPACE_TOO_SMALL)
+    assert ekv.ekv_status_string(99) == "unknown status"
+
+
+def _kv(hkv=8, d=128, page=16, n_t=0, n_c=100):
+    return ekv.PagedKV(FAKE if n_t else None, FAKE if n_t else None, n_t,
+                       FAKE if n_c else None, FAKE if n_c else None, FAKE if n_c else None, n_c,
+                       hkv, d, page)
+
+
+def _decode(kv, hq=32, batch=4, pt_stride=512, fidelity=FAKE, max_len=8192, scratch=FAKE,
+            scratch_bytes=1 << 30, pps=0, out_dtype=0, q=FAKE):
+    return ekv._lib.ekv_decode_attention(ctypes.byref(kv) if kv is not None else None, q, batch, hq,
+                                         FAKE, pt_stride, fidelity, FAKE, max_len, 0.088, FAKE,
+                                         out_dtype, None, pps, scratch, scratch_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(hq=30), ekv.EKV_ERR_INVALID_ARG),          # Hq % Hkv != 0
+    (dict(hq=24), ekv.EKV_ERR_UNSUPPORTED),          # G = 3
+    (dict(pt_stride=100), ekv.EKV_ERR_INVALID_ARG),  # stride < ceil(max_len / 16)
+    (dict(scratch=None), ekv.EKV_ERR_INVALID_ARG),
+    (dict(scratch_bytes=16), ekv.EKV_ERR_INVALID_ARG),
+    (dict(scratch=FAKE + 16), ekv.EKV_ERR_INVALID_ARG),  # scratch not 256-byte aligned
+    (dict(pps=5000), ekv.EKV_ERR_INVALID_ARG),
+    (dict(out_dtype=7), ekv.EKV_ERR_INVALID_ARG),
+    (dict(q=None), ekv.EKV_ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), ekv.EKV_ERR_INVALID_ARG),     # misaligned query
+])
+def test_decode_validation(kwargs, status):
+    assert _decode(_kv(), **kwargs) == status
+    assert ekv.ekv_last_error() != ""
+
+
+def test_decode_validation_of_pools():
+    assert _decode(None) == ekv.EKV_ERR_INVALID_ARG
+    assert _decode(_kv(d=96)) == ekv.EKV_ERR_UNSUPPORTED
+    assert _decode(_kv(page=8)) == ekv.EKV_ERR_INVALID_ARG
+    assert _decode(_kv(n_t=5, n_c=5), fidelity=None) == ekv.EKV_ERR_INVALID_ARG
+    bad = _kv()
+    bad.v_scale = None
+    assert _decode(bad) == ekv.EKV_ERR_INVALID_ARG
+
+
+def test_decode_empty_batch_is_ok_without_launch():
+    assert _decode(_kv(), batch=0) == ekv.EKV_OK
+    assert ekv.ekv_last_error() == ""
+
+
+def test_split_plan_and_scratch_size():
+    pps = ekv.ekv_decode_pages_per_split(32, 8, 8192)
+    assert pps in (16, 32, 64, 128, 256, 512)
+    splits = -(-512 // pps)
+    rows = 32 * 32 * splits
+    acc = rows * 128 * 4
+    expect = ((acc + 255) // 256) * 256 + rows * 2 * 4
+    assert ekv.ekv_decode_scratch_bytes(32, 32, 8, 128, 8192, 0) == expect
+    assert ekv.ekv_decode_scratch_bytes(2, 4, 1, 64, 64, 1) == ((2 * 4 * 4 * 64 * 4 + 255) // 256) * 256 + 2 * 4 * 4 * 8
+    assert ekv.ekv_decode_scratch_bytes(0, 4, 1, 64, 64, 1) == 0
+
+
+def test_gather_validation():
+    kv = _kv()
+    g = ekv._lib.ekv_gather_compact_pages
+    assert g(ctypes.byref(kv), FAKE, 4097, 1, FAKE, FAKE, 4096, None) == ekv.EKV_ERR_WORKSPACE_TOO_SMALL
+    assert g(ctypes.byref(kv), FAKE, 4, 2, FAKE, FAKE, 4096, None) == ekv.EKV_ERR_INVALID_ARG
+    assert g(ctypes.byref(kv), None, 4, 1, FAKE, FAKE, 4096, None) == ekv.EKV_ERR_INVALID_ARG
+    assert g(ctypes.byref(_kv(d=32)), FAKE, 4, 1, FAKE, FAKE, 4096, None) == ekv.EKV_ERR_UNSUPPORTED
+    no_c = _kv(n_t=4, n_c=0)
+    assert g(ctypes.byref(no_c), FAKE, 4, 1, FAKE, FAKE, 4096, None) == ekv.EKV_ERR_INVALID_ARG
+    assert g(ctypes.byref(kv), FAKE, 0, 1, FAKE, FAKE, 4096, None) == ekv.EKV_OK
+
+
+def _prefill(max_len=8192, hq=32, hkv=8, d=128, causal=1, out=FAKE):
+    return ekv._lib.ekv_prefill_attention(FAKE, 1000, FAKE, FAKE, 1000, FAKE, FAKE, 2, max_len, hq,
+                                          hkv, d, causal, 0.088, out, 0, None, None)
+
+
+def test_prefill_validation():
+    assert _prefill(max_len=8193) == ekv.EKV_ERR_NOT_ELIGIBLE
+    assert _prefill(hq=33) == ekv.EKV_ERR_INVALID_ARG
+    assert _prefill(d=80) == ekv.EKV_ERR_UNSUPPORTED
+    assert _prefill(causal=2) == ekv.EKV_ERR_INVALID_ARG
+    assert _prefill(out=None) == ekv.EKV_ERR_INVALID_ARG
+    assert _prefill(max_len=0) == ekv.EKV_OK
+
+
+def test_e4m3_diagnostic_validation():
+    f = ekv._lib.ekv_e4m3_to_f16
+    assert f(FAKE, 4, FAKE, 3, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(None, 4, FAKE, 0, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(FAKE, 0, FAKE, 0, None) == ekv.EKV_OK

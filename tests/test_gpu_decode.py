@@ -1,0 +1,151 @@
+"""GPU parity: mixed-fidelity paged decode vs the float64 oracle (max-abs <= 2e-3)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (TOL, DeviceCase, assert_close, assert_lse_close, dev, ekv,
+                         f16_bits_equal_rne, max_abs, oracle_decode, step)
+from mixed_precision_paged_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+LENS = [1, 15, 16, 17, 37, 64, 300, 1000, 2053]
+
+
+def test_tiny_decode_case():
+    step("decode tiny")
+    c = synth.tiny_decode_case()
+    dc = DeviceCase(c)
+    want, wlse = oracle_decode(c)
+    out32, lse = dc.decode(torch.float32)
+    assert_close(out32, want)
+    assert_lse_close(lse, wlse)
+    out16, _ = dc.decode(torch.float16)
+    assert f16_bits_equal_rne(out16, out32)
+    out_nf, _ = dc.decode(torch.float32, flags=False)  # uniform-pool path (no flag reads)
+    np.testing.assert_array_equal(out_nf, out32)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 128), (16, 8, 64), (4, 2, 64), (8, 1, 128)])
+def test_mixed_fidelity_ragged(hq, hkv, d):
+    step(f"decode mixed hq={hq} hkv={hkv} d={d}")
+    c = synth.make_paged_case(100 + hq + d, LENS, hq, hkv, d, compact_frac=0.3,
+                              outlier_frac=0.01, outlier_mult=20.0)
+    dc = DeviceCase(c)
+    want, wlse = oracle_decode(c)
+    out, lse = dc.decode(torch.float32)
+    assert_close(out, want)
+    assert_lse_close(lse, wlse)
+
+
+@pytest.mark.parametrize("frac", [0.0, 1.0])
+def test_single_kind_batches(frac):
+    step(f"decode single kind frac={frac}")
+    c = synth.make_paged_case(7, LENS, 32, 8, 128, compact_frac=frac)
+    dc = DeviceCase(c)
+    want, wlse = oracle_decode(c)
+    out, lse = dc.decode(torch.float32)
+    assert_close(out, want)
+    assert_lse_close(lse, wlse)
+    out_nf, _ = dc.decode(torch.float32, flags=False)
+    np.testing.assert_array_equal(out_nf, out)
+
+
+def test_split_count_does_not_change_the_result():
+    step("decode split counts")
+    c = synth.make_paged_case(8, [2053, 700, 33], 32, 8, 128, compact_frac=0.5)
+    dc = DeviceCase(c)
+    want, wlse = oracle_decode(c)
+    outs = []
+    for pps in (1, 3, 16, 64, 0, 4096):
+        out, lse = dc.decode(torch.float32, pages_per_split=pps)
+        assert_close(out, want, what=f"pages_per_split={pps}")
+        assert_lse_close(lse, wlse)
+        outs.append(out)
+    for o in outs[1:]:
+        assert max_abs(o, outs[0]) <= TOL
+
+
+def test_page_permutation_gives_identical_output():
+    step("decode page permutation")
+    c = synth.make_paged_case(9, [300, 129], 8, 2, 128, compact_frac=0.5, slack_frac=0.5)
+    dc = DeviceCase(c)
+    out1, lse1 = dc.decode(torch.float32, pages_per_split=4)
+    # move every page to a new physical slot in both pools and rewrite the table
+    rng = np.random.default_rng(1)
+    c2 = synth.PagedCase(**{f: getattr(c, f) for f in c.__dataclass_fields__})
+    pt = c.page_table.copy()
+    for kind, names in ((0, ("k_target", "v_target")), (1, ("k_compact", "v_compact", "v_scale"))):
+        P = getattr(c, names[0]).shape[0]
+        perm = rng.permutation(P)
+        inv = np.empty(P, np.int64)
+        inv[perm] = np.arange(P)
+        for n in names:
+            setattr(c2, n, getattr(c, n)[perm])
+        mask = c.fidelity == kind
+        pt[mask] = inv[c.page_table[mask]]
+    c2.page_table = pt
+    assert not np.array_equal(pt, c.page_table)
+    out2, lse2 = DeviceCase(c2).decode(torch.float32, pages_per_split=4)
+    np.testing.assert_array_equal(out1, out2)
+    np.testing.assert_array_equal(lse1, lse2)
+
+
+def test_compact_page_with_exact_values_equals_target_page():
+    step("decode compact==target")
+    c = synth.make_paged_case(10, [200, 45], 8, 2, 64, compact_frac=1.0)
+    # TARGET copy of every compact page with V = e4m3 value exactly (scale 1)
+    c.v_scale[:] = 1.0
+    vals = torch.from_numpy(c.v_compact).view(torch.float8_e4m3fn).to(torch.float16).numpy()
+    ct = synth.PagedCase(**{f: getattr(c, f) for f in c.__dataclass_fields__})
+    ct.k_target, ct.v_target = c.k_compact.copy(), vals
+    ct.k_compact = c.k_compact[:0]
+    ct.v_compact, ct.v_scale = c.v_compact[:0], c.v_scale[:0]
+    ct.fidelity = np.zeros_like(c.fidelity)
+    oc, lc = DeviceCase(c).decode(torch.float32)
+    ot, lt = DeviceCase(ct).decode(torch.float32)
+    np.testing.assert_array_equal(oc, ot)
+    np.testing.assert_array_equal(lc, lt)
+
+
+def test_empty_sequences_and_bad_pages():
+    step("decode empty and bad pages")
+    c = synth.make_paged_case(11, [40, 40, 40], 8, 2, 128, compact_frac=0.5)
+    dc = DeviceCase(c)
+    lens = c.seq_lens.copy()
+    lens[1] = 0
+    out, lse = dc.decode(torch.float32, seq_lens=dev(lens))
+    want, wlse = oracle_decode(c, seq_lens=lens)
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+    assert_close(out[[0, 2]], want[[0, 2]])
+    bad = c.page_table.copy()
+    bad[2, 1] = 1 << 20  # out of range for either pool
+    dc.page_table = dev(bad)
+    out, lse = dc.decode(torch.float32)
+    assert np.all(np.isnan(out[2])) and np.all(np.isnan(lse[2]))
+    assert_close(out[:2], oracle_decode(c)[0][:2])
+    badf = c.fidelity.copy()
+    badf[0, 0] = 2
+    dc.page_table, dc.fidelity = dev(c.page_table), dev(badf)
+    out, _ = dc.decode(torch.float32)
+    assert np.all(np.isnan(out[0])) and np.all(np.isfinite(out[1:]))
+
+
+def test_planted_oracle_mistakes_are_detected():
+    """Plant one wrong scale / page id / flag in the ORACLE's copy: parity must fail."""
+    step("decode fault injection")
+    c = synth.make_paged_case(12, [64, 64], 8, 2, 128, compact_frac=0.5)
+    out, _ = DeviceCase(c).decode(torch.float32)
+    assert max_abs(out, oracle_decode(c)[0]) <= TOL
+    comp0 = np.flatnonzero(c.fidelity[0, :4] == 1)
+    comp1 = np.flatnonzero(c.fidelity[1, :4] == 1)
+    targ0 = np.flatnonzero(c.fidelity[0, :4] == 0)
+    assert comp0.size and comp1.size and targ0.size
+    sc = c.v_scale.copy()
+    sc[c.page_table[0, comp0[0]]] *= 1.5                      # one wrong scale
+    pt = c.page_table.copy()
+    pt[0, comp0[0]], pt[1, comp1[0]] = pt[1, comp1[0]], pt[0, comp0[0]]  # two ids exchanged
+    pt2, fl2 = c.page_table.copy(), c.fidelity.copy()
+    pt2[0, targ0[0]], fl2[0, targ0[0]] = c.page_table[1, comp1[0]], 1   # one flag flipped
+    for kwargs in (dict(v_scale=sc), dict(page_table=pt), dict(page_table=pt2, fidelity=fl2)):
+        assert max_abs(out, oracle_decode(c, **kwargs)[0]) > TOL, list(kwargs)

@@ -1,0 +1,88 @@
+"""GPU parity: device E4M3 decoding and the compact-page gather (bit-exact)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import DeviceCase, dev, ekv, step
+from mixed_precision_paged_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("method,scale", [(0, 1.0), (1, 1.0), (2, 2.0 ** -7)])
+def test_device_e4m3_matches_oracle_table(method, scale):
+    """Every code in every byte position of a packed word (codes run 0..255 four times,
+    shifted by one each pass)."""
+    step(f"e4m3 table method {method}")
+    codes_np = np.concatenate([np.roll(np.arange(256, dtype=np.uint8), k) for k in range(4)])
+    codes = dev(codes_np)
+    out = torch.empty(codes_np.size, dtype=torch.float16, device="cuda")
+    ekv().ekv_e4m3_to_f16(codes, out, method)
+    got = out.cpu().numpy()
+    want = (oracle.E4M3FN_TABLE[codes_np] * scale).astype(np.float16)
+    nan = np.isnan(want)
+    assert np.all(np.isnan(got[nan]))
+    bad = np.flatnonzero(got.view(np.uint16)[~nan] != want.view(np.uint16)[~nan])
+    assert bad.size == 0, [(int(codes_np[~nan][i]), float(got[~nan][i]), float(want[~nan][i])) for i in bad[:8]]
+
+
+def _gather_gpu(dc, ids, apply_scale, capacity=None):
+    c = dc.case
+    n = len(ids)
+    cap = n if capacity is None else capacity
+    ws_k = torch.full((cap, 16, c.num_kv_heads, c.head_dim), 7.0, dtype=torch.float16, device="cuda")
+    ws_v = torch.full_like(ws_k, 7.0)
+    ekv().ekv_gather_compact_pages(dc.kv(), dev(np.asarray(ids, np.int32)), apply_scale, ws_k, ws_v)
+    torch.cuda.synchronize()
+    return ws_k.cpu().numpy(), ws_v.cpu().numpy()
+
+
+def _assert_bits(got, want):
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got.view(np.uint16)[~nan], want.view(np.uint16)[~nan])
+
+
+@pytest.mark.parametrize("apply_scale", [False, True])
+def test_gather_tiny_pool_all_pages(apply_scale):
+    step(f"gather tiny apply_scale={apply_scale}")
+    c = synth.tiny_decode_case()
+    dc = DeviceCase(c)
+    ids = np.arange(16, dtype=np.int32)  # every pool page, including NaN-poisoned ones
+    gk, gv = _gather_gpu(dc, ids, apply_scale)
+    ok, ov = oracle.gather_compact_pages(c.k_compact, c.v_compact, c.v_scale, ids, apply_scale)
+    _assert_bits(gk, ok)
+    _assert_bits(gv, ov)
+
+
+@pytest.mark.parametrize("hkv,d", [(8, 128), (2, 64), (1, 128)])
+@pytest.mark.parametrize("apply_scale", [False, True])
+def test_gather_ragged_pages_with_repeats(hkv, d, apply_scale):
+    step(f"gather ragged hkv={hkv} d={d} scale={apply_scale}")
+    c = synth.make_paged_case(41, [37, 300, 1001, 16], 4 * hkv, hkv, d, compact_frac=1.0)
+    dc = DeviceCase(c)
+    rng = np.random.default_rng(5)
+    ids = rng.integers(0, c.k_compact.shape[0], size=97).astype(np.int32)
+    ids[:3] = ids[3]  # repeated page ids are legal
+    gk, gv = _gather_gpu(dc, ids, apply_scale, capacity=128)
+    ok, ov = oracle.gather_compact_pages(c.k_compact, c.v_compact, c.v_scale, ids, apply_scale)
+    _assert_bits(gk[:97], ok)
+    _assert_bits(gv[:97], ov)
+    assert np.all(gk[97:] == 7.0) and np.all(gv[97:] == 7.0)  # capacity tail untouched
+
+
+def test_gather_rejects_overflow_and_marks_bad_ids():
+    step("gather errors")
+    c = synth.make_paged_case(42, [64], 8, 2, 64, compact_frac=1.0)
+    dc = DeviceCase(c)
+    ws = torch.zeros((2, 16, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(ekv().EkvError) as e:
+        ekv().ekv_gather_compact_pages(dc.kv(), dev(np.zeros(3, np.int32)), True, ws, ws.clone())
+    assert e.value.status == ekv().EKV_ERR_WORKSPACE_TOO_SMALL
+    ids = np.array([0, c.k_compact.shape[0] + 5], np.int32)
+    gk, gv = _gather_gpu(dc, ids, True)
+    assert np.all(np.isnan(gk[1])) and np.all(np.isnan(gv[1]))
+    ok, ov = oracle.gather_compact_pages(c.k_compact, c.v_compact, c.v_scale, ids[:1], True)
+    _assert_bits(gk[:1], ok)
+    _assert_bits(gv[:1], ov)

@@ -1,0 +1,141 @@
+"""GPU parity: compact-prefill route (gather -> causal FP16 MFMA prefill) vs the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (TOL, DeviceCase, assert_close, assert_lse_close, dev, ekv,
+                         f16_bits_equal_rne, max_abs, oracle_decode, step)
+from mixed_precision_paged_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _v_ratio(ws_v):
+    """|V| of a workspace relative to N(0,1) data (whose page absmax is about 4)."""
+    v = np.asarray(ws_v, dtype=np.float64)
+    return max(1.0, float(np.nanmax(np.abs(v))) / 4.0)
+
+
+def _route(pc, prompts, apply_scale=True, out_dtype=torch.float32, causal=True, capacity=None):
+    """GPU: gather the prompts' pages, then prefill.  Returns (out, lse, ws_k, ws_v) on host."""
+    c = pc.paged
+    dc = DeviceCase(c)
+    ids, kv_start = pc.chunk_pages(prompts)
+    cap = len(ids) if capacity is None else capacity
+    ws_k = torch.empty((cap, 16, c.num_kv_heads, c.head_dim), dtype=torch.float16, device="cuda")
+    ws_v = torch.empty_like(ws_k)
+    ekv().ekv_gather_compact_pages(dc.kv(), dev(ids), apply_scale, ws_k, ws_v)
+    rows = np.concatenate([np.arange(pc.cu_seqlens_q[p], pc.cu_seqlens_q[p + 1]) for p in prompts])
+    q = dev(c.q[rows])
+    lens = pc.prompt_lens[list(prompts)]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    out = torch.full((len(rows), c.num_q_heads, c.head_dim), 5.0, dtype=out_dtype, device="cuda")
+    lse = torch.empty((len(rows), c.num_q_heads), dtype=torch.float32, device="cuda")
+    ekv().ekv_prefill_attention(q, ws_k, ws_v, dev(cu), dev(kv_start), int(lens.max()), c.sm_scale,
+                                out, lse, causal=causal)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), ws_k.cpu().numpy(), ws_v.cpu().numpy(), rows, cu, kv_start
+
+
+def _oracle_route(pc, prompts, rows, cu, kv_start, apply_scale=True, causal=True, sample=None):
+    c = pc.paged
+    ids, _ = pc.chunk_pages(prompts)
+    wk, wv = oracle.gather_compact_pages(c.k_compact, c.v_compact, c.v_scale, ids, apply_scale)
+    wk = wk.reshape(-1, c.num_kv_heads, c.head_dim)
+    wv = wv.reshape(-1, c.num_kv_heads, c.head_dim)
+    return oracle.prefill_attention(c.q[rows], wk, wv, cu, kv_start, causal, c.sm_scale, rows=sample)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (8, 2, 128), (16, 2, 64)])
+def test_prefill_route_ragged_prompts(hq, hkv, d):
+    step(f"prefill ragged hq={hq} hkv={hkv} d={d}")
+    lens = [1, 17, 100, 257, 64, 130]
+    pc = synth.make_prefill_case(200 + d + hq, lens, hq, hkv, d)
+    prompts = list(range(len(lens)))
+    out, lse, *_, rows, cu, ks = _route(pc, prompts)
+    want, wlse = _oracle_route(pc, prompts, rows, cu, ks)
+    assert_close(out, want)
+    assert_lse_close(lse, wlse)
+
+
+def test_prefill_fp16_output_is_rne_of_fp32_and_noncausal():
+    step("prefill fp16 + noncausal")
+    pc = synth.make_prefill_case(301, [200, 77], 32, 8, 128)
+    out32, *_ = _route(pc, [0, 1])
+    out16, *_ = _route(pc, [0, 1], out_dtype=torch.float16)
+    assert f16_bits_equal_rne(out16, out32)
+    out, lse, *_, rows, cu, ks = _route(pc, [0, 1], causal=False)
+    want, wlse = _oracle_route(pc, [0, 1], rows, cu, ks, causal=False)
+    assert_close(out, want)
+    assert_lse_close(lse, wlse)
+
+
+def test_prefill_unscaled_gather_route():
+    step("prefill unscaled route")
+    pc = synth.make_prefill_case(302, [150, 33], 8, 2, 128)
+    out, lse, wk, wv, rows, cu, ks = _route(pc, [1, 0], apply_scale=False)
+    want, wlse = _oracle_route(pc, [1, 0], rows, cu, ks, apply_scale=False)
+    # unscaled values are E4M3 codes (|v| up to 448, not N(0,1)): the bound scales with |V|
+    assert_close(out, want, tol=TOL * _v_ratio(wv))
+    assert_lse_close(lse, wlse)
+
+
+def test_prefill_over_arbitrary_workspace_rows():
+    """Prompts placed at gaps of NaN rows in K/V: only their own rows may be read."""
+    step("prefill arbitrary rows")
+    rng = np.random.default_rng(3)
+    hq, hkv, d = 16, 4, 128
+    lens = [5, 129, 300]
+    starts, r = [], 0
+    for n in lens:
+        r += 7
+        starts.append(r)
+        r += n
+    k = np.full((r + 9, hkv, d), np.nan, np.float16)
+    v = np.full((r + 9, hkv, d), np.nan, np.float16)
+    for s, n in zip(starts, lens):
+        k[s:s + n] = rng.standard_normal((n, hkv, d))
+        v[s:s + n] = rng.standard_normal((n, hkv, d))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = rng.standard_normal((cu[-1], hq, d)).astype(np.float16)
+    out = torch.empty((cu[-1], hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cu[-1], hq), dtype=torch.float32, device="cuda")
+    sm = 1 / np.sqrt(d)
+    ekv().ekv_prefill_attention(dev(q), dev(k), dev(v), dev(cu), dev(np.array(starts, np.int32)),
+                                max(lens), sm, out, lse)
+    torch.cuda.synchronize()
+    want, wlse = oracle.prefill_attention(q, k, v, cu, starts, True, sm)
+    assert_close(out.cpu().numpy(), want)
+    assert_lse_close(lse.cpu().numpy(), wlse)
+
+
+def test_prefill_bad_offsets_give_nan_rows_not_faults():
+    step("prefill bad offsets")
+    hq, hkv, d = 8, 2, 64
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((100, hkv, d)).astype(np.float16)
+    q = rng.standard_normal((60, hq, d)).astype(np.float16)
+    cu = np.array([0, 30, 60], np.int32)
+    starts = np.array([0, 90], np.int32)  # second prompt would read rows 90..119 of 100
+    out = torch.zeros((60, hq, d), dtype=torch.float32, device="cuda")
+    ekv().ekv_prefill_attention(dev(q), dev(k), dev(k), dev(cu), dev(starts), 30, 0.125, out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o[:30])) and np.all(np.isnan(o[30:]))
+
+
+def test_prefill_row_equals_decode_over_prefix():
+    """Cross-kernel: prefill row i over a prompt == decode over its first i+1 tokens."""
+    step("prefill vs decode prefix")
+    pc = synth.make_prefill_case(303, [77], 32, 8, 128)
+    pc.paged.v_scale[:] = 1.0  # unit scales: the unscaled workspace holds the decode values
+    out, lse, wk, wv, *_ = _route(pc, [0], apply_scale=False)
+    tol = 2 * TOL * _v_ratio(wv)  # unit scales: |V| up to 448
+    dc = DeviceCase(pc.paged)
+    for i in (0, 15, 16, 63, 76):
+        q = dev(pc.paged.q[i:i + 1])
+        lens = dev(np.array([i + 1], np.int32))
+        od, ld = dc.decode(torch.float32, q=q, rows=[0], seq_lens=lens, max_seq_len=77)
+        assert max_abs(out[i], od[0]) <= tol
+        assert abs(float(lse[i, 0]) - float(ld[0, 0])) <= 2 * TOL

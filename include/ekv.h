@@ -75,7 +75,8 @@ typedef enum { EKV_F16 = 0, EKV_F32 = 1 } ekv_dtype;
  *   v_compact          : u8 E4M3FN [n_compact_pages][16][num_kv_heads][head_dim]
  *   v_scale            : fp32 [n_compact_pages][num_kv_heads]; the value of a
  *                        compact element is e4m3(byte) * v_scale[page][head]
- * A pool that is not used may be NULL with its page count 0.
+ * A pool that is not used may be NULL with its page count 0.  Page counts
+ * must be below 2^30.  Scales must be positive normal fp32 values.
  */
 typedef struct {
   const void* k_target;
@@ -139,7 +140,7 @@ size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_
  *              value is the round-to-nearest-even of the EKV_F32 result.
  *   lse        optional fp32 [batch][num_q_heads]: natural-log normalizer
  *              max_t s_t + ln sum_t exp(s_t - max_t s_t).
- *   pages_per_split  split-K granularity (0 = automatic; else 1..4096).
+ *   pages_per_split  split-K granularity (0 = automatic; else 1..512).
  *   scratch    device buffer of at least ekv_decode_scratch_bytes(...) bytes
  *              (same arguments), 256-byte aligned; contents are overwritten.
  * Sequences that reference an out-of-range page id or an unknown flag get

@@ -42,88 +42,100 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr float kTau = 8.0f;          // deferred-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;   // "no token yet" running max
+constexpr bool kHeadMajorGrid = true; // launch order: the KV heads of one (sequence, split) adjacent
+constexpr int kMaxSplitPages = 512;   // pages per split (metadata staged in LDS)
 
 template <int D>
 struct PageRegs {
-  uint32_t k[2][D / 16];  // two tokens x (D/8 fp16) of this lane's d-set
-  uint32_t v[2][D / 16];  // TARGET: same as k; COMPACT: first D/32 dwords hold D/8 E4M3 bytes
+  f16x8 k[D / 32];        // K[token lane%16][32kb + 8(lane/16) .. +8]: MFMA B operand per kb
+  uint32_t v[2][D / 16];  // V rows of tokens tp, tp+8 at this lane's d-set (TARGET fp16;
+                          // COMPACT: the first D/32 dwords hold D/8 E4M3 bytes)
 };
 
+// One prefetch slot: a page's K/V registers plus its uniform metadata.
 template <int D>
-__device__ __forceinline__ void load_page(PageRegs<D>& r, const DecodeParams& p, int kind,
-                                          int phys, int g, int tp, int j) {
+struct Slot {
+  PageRegs<D> r;
+  int kind;
+  float scale;
+  bool ok;
+};
+
+// Loads one page's K and V rows of this lane with buffer loads.  The buffer
+// descriptors (wavefront-uniform, SGPRs) cover exactly one page of one KV head,
+// so the hardware range check keeps every access inside that page; `koff`/
+// `voff` are per-lane 32-bit byte offsets (token tp, d-octet j) and the
+// second token's 8-row stride goes in the scalar offset.
+template <int D>
+__device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* kbase,
+                                          const char* vbase, uint32_t kbytes, uint32_t vbytes,
+                                          uint32_t kqoff, uint32_t koff, uint32_t voff,
+                                          uint32_t krow8, uint32_t vrow8) {
   constexpr int NC = D / 64;
-  const int64_t row = (int64_t)p.num_kv_heads * D;  // elements per token row of a page
-  const int64_t base = (int64_t)phys * kPage * row + (int64_t)g * D;
-  const uint16_t* kp = (kind ? p.k_compact : p.k_target) + base;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, kbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, vbytes, kBufferFlags);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int64_t off = (int64_t)(tp + 8 * t) * row + 8 * j;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint4 x = *reinterpret_cast<const uint4*>(kp + off + 64 * c);
-      r.k[t][4 * c + 0] = x.x; r.k[t][4 * c + 1] = x.y;
-      r.k[t][4 * c + 2] = x.z; r.k[t][4 * c + 3] = x.w;
-    }
-  }
+  for (int kb = 0; kb < D / 32; ++kb)
+    r.k[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, kqoff + 64u * kb, 0, 0));
   if (kind == 0) {
-    const uint16_t* vp = p.v_target + base;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t off = (int64_t)(tp + 8 * t) * row + 8 * j;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vp + off + 64 * c);
-        r.v[t][4 * c + 0] = x.x; r.v[t][4 * c + 1] = x.y;
-        r.v[t][4 * c + 2] = x.z; r.v[t][4 * c + 3] = x.w;
+        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vr, koff + 128u * c, t * krow8, 0);
+        r.v[t][4 * c + 0] = y.x; r.v[t][4 * c + 1] = y.y;
+        r.v[t][4 * c + 2] = y.z; r.v[t][4 * c + 3] = y.w;
       }
-    }
   } else {
-    const uint8_t* vp = p.v_compact + base;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t off = (int64_t)(tp + 8 * t) * row + 8 * j;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint2 x = *reinterpret_cast<const uint2*>(vp + off + 64 * c);
-        r.v[t][2 * c + 0] = x.x; r.v[t][2 * c + 1] = x.y;
+        const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 64u * c, t * vrow8, 0);
+        r.v[t][2 * c + 0] = y.x; r.v[t][2 * c + 1] = y.y;
       }
-    }
+    // keep every element of the register array defined on both paths (no scratch)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int w = D / 32; w < D / 16; ++w) r.v[t][w] = 0u;
   }
 }
 
 template <int D, int G>
 struct State {
-  uint32_t q[G][D / 16];   // fp16 pairs of the lane's d-set, per query head of the group
+  f16x8 qa[D / 32];  // Q[head lane%16][32kb + 8(lane/16) .. +8]: MFMA A operand (0 for head >= G)
   float m[G], l[G];
   float acc[G][D / 8];
 };
 
 template <int D, int G>
 __device__ __forceinline__ void process_page(State<D, G>& st, PageRegs<D>& r, const DecodeParams& p,
-                                             int kind, int phys, int g, int pg, int len, int tp) {
+                                             int kind, float scale, int pg, int len, int tp) {
   constexpr int DW = D / 16;
   // Compact scale s = 2^e * f, f in [1, 2): the conversion applies the exact power of two,
   // p carries f.  (Scales are positive normal fp32 values.)
-  const uint32_t sbits = kind ? __builtin_bit_cast(uint32_t, p.v_scale[(int64_t)phys * p.num_kv_heads + g])
-                              : 0x3F800000u;
+  const uint32_t sbits = kind ? __builtin_bit_cast(uint32_t, scale) : 0x3F800000u;
   const float s_pow2 = as_f32(sbits & 0x7F800000u);
   const float s_frac = as_f32((sbits & 0x807FFFFFu) | 0x3F800000u);
   const int t0 = pg * kPage + tp;
   const bool ok0 = t0 < len, ok1 = t0 + 8 < len;
   const bool partial = pg * kPage + kPage > len;  // wavefront-uniform
 
+  // S[h][t] = Q . K^T on the matrix cores: rows = heads (padded to 16), columns = the
+  // page's 16 tokens; lane l receives S[4(l/16)+i][l%16], i < 4.
+  f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb)
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.qa[kb], r.k[kb], sacc, 0, 0, 0);
+  // Move the scores of tokens tp and tp+8 to this lane (PV layout).
   float s0[G], s1[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < DW; ++w) {
-      a0 = dot2(st.q[h][w], r.k[0][w], a0);
-      a1 = dot2(st.q[h][w], r.k[1][w], a1);
-    }
-    s0[h] = octet_sum(a0) * p.scale_log2;
-    s1[h] = octet_sum(a1) * p.scale_log2;
+    const int src = 16 * (h / 4);
+    const float v = sacc[h % 4];
+    s0[h] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (src + tp), __builtin_bit_cast(int, v))) * p.scale_log2;
+    s1[h] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (src + tp + 8), __builtin_bit_cast(int, v))) * p.scale_log2;
   }
   if (partial) {  // last page of the sequence: drop slots >= len (their contents are undefined)
     const float ninf = -__builtin_inff();
@@ -208,11 +220,15 @@ __global__ __launch_bounds__(kThreads, (G * D >= 1024 ? 1 : 2)) void decode_spli
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ int s_bad[kWaves];
+  __shared__ int s_meta[kMaxSplitPages];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  // wavefront index made provably uniform, so page metadata becomes scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int j = lane & 7, tp = lane >> 3;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int split = kHeadMajorGrid ? blockIdx.y : blockIdx.x;
+  const int g = kHeadMajorGrid ? blockIdx.x : blockIdx.y;
+  const int b = blockIdx.z;
   const int len = min(max(p.seq_lens[b], 0), p.max_seq_len);
   const int npages = (len + kPage - 1) / kPage;
   const int pbeg = split * p.pages_per_split;
@@ -220,60 +236,75 @@ __global__ __launch_bounds__(kThreads, (G * D >= 1024 ? 1 : 2)) void decode_spli
   const int pend = min(pbeg + p.pages_per_split, npages);
 
   State<D, G> st;
+  {
+    const int qh = lane & 15, qc = lane >> 4;
+    const uint16_t* qp = p.q + ((int64_t)b * p.num_q_heads + g * G + qh) * D + 8 * qc;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb)
+      st.qa[kb] = qh < G ? __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(qp + 32 * kb)) : f16x8{};
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const uint16_t* qp = p.q + ((int64_t)b * p.num_q_heads + g * G + h) * D + 8 * j;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint4 x = *reinterpret_cast<const uint4*>(qp + 64 * c);
-      st.q[h][4 * c + 0] = x.x; st.q[h][4 * c + 1] = x.y;
-      st.q[h][4 * c + 2] = x.z; st.q[h][4 * c + 3] = x.w;
-    }
     st.m[h] = kNegBig;
     st.l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < DE; ++e) st.acc[h][e] = 0.f;
   }
 
-  const int32_t* pt = p.page_table + (int64_t)b * p.pt_stride;
-  const uint8_t* fl = FLAGS ? p.fidelity + (int64_t)b * p.pt_stride : nullptr;
+  // Stage this split's page metadata in LDS once: (phys << 1 | kind), or -1
+  // for an out-of-range id or unknown flag.  Per-page reads are then LDS
+  // reads, which never wait on the vector-memory counter of in-flight pages.
+  {
+    const int32_t* pt = p.page_table + (int64_t)b * p.pt_stride;
+    const uint8_t* fl = FLAGS ? p.fidelity + (int64_t)b * p.pt_stride : nullptr;
+    for (int i = threadIdx.x; i < pend - pbeg; i += kThreads) {
+      const int phys = pt[pbeg + i];
+      const int kind = FLAGS ? (int)fl[pbeg + i] : p.uniform_kind;
+      const bool ok = (kind == 0 && (unsigned)phys < (unsigned)p.n_target) ||
+                      (kind == 1 && (unsigned)phys < (unsigned)p.n_compact);
+      s_meta[i] = ok ? (phys << 1) | kind : -1;
+    }
+  }
+  __syncthreads();
+
+  // Per-lane byte offsets inside a page (token tp, d-octet j) and 8-row strides.
+  const uint32_t krow = (uint32_t)p.num_kv_heads * D * 2u;   // bytes per token row, fp16
+  const uint32_t vrow = (uint32_t)p.num_kv_heads * D;        // bytes per token row, E4M3
+  const uint32_t koff = (uint32_t)tp * krow + 16u * j;          // V16 rows (PV layout)
+  const uint32_t kqoff = (uint32_t)(lane & 15) * krow + 16u * (lane >> 4);  // K rows (MFMA layout)
+  const uint32_t voff = (uint32_t)tp * vrow + 8u * j;
+  const int64_t kpage = (int64_t)kPage * krow, vpage8 = (int64_t)kPage * vrow;
   bool bad = false;
 
-  auto meta = [&](int pg, int& kind, int& phys) -> bool {
-    phys = pt[pg];
-    kind = FLAGS ? (int)fl[pg] : p.uniform_kind;
-    if (kind == 0) return (unsigned)phys < (unsigned)p.n_target;
-    if (kind == 1) return (unsigned)phys < (unsigned)p.n_compact;
-    return false;
+  auto issue = [&](Slot<D>& sl, int pq) {
+    sl.ok = false;
+    if (pq >= pend) return;
+    const int m = __builtin_amdgcn_readfirstlane(s_meta[pq - pbeg]);
+    if (m < 0) { bad = true; return; }
+    const int phys = m >> 1;
+    sl.kind = m & 1;
+    sl.ok = true;
+    const char* kb = reinterpret_cast<const char*>(sl.kind ? p.k_compact : p.k_target) +
+                     phys * kpage + (int64_t)g * D * 2;
+    const char* vb = sl.kind ? reinterpret_cast<const char*>(p.v_compact) + phys * vpage8 + (int64_t)g * D
+                             : reinterpret_cast<const char*>(p.v_target) + phys * kpage + (int64_t)g * D * 2;
+    const uint32_t kbytes = (uint32_t)kpage - (uint32_t)g * D * 2;
+    const uint32_t vbytes = sl.kind ? (uint32_t)vpage8 - (uint32_t)g * D : kbytes;
+    sl.scale = sl.kind ? p.v_scale[(int64_t)phys * p.num_kv_heads + g] : 1.0f;
+    load_page<D>(sl.r, sl.kind, kb, vb, kbytes, vbytes, kqoff, koff, voff, 8u * krow, 8u * vrow);
   };
-
-  // Two register buffers: the next page loads while the current one computes.
-  PageRegs<D> ra, rb;
-  int ka = 0, pa = 0, kb = 0, pb = 0;
-  bool oka = false, okb = false;
+  // Two slots: page pg+4 loads while page pg computes.
+  Slot<D> sa, sb;
   int pg = pbeg + wave;
-  if (pg < pend) {
-    oka = meta(pg, ka, pa);
-    if (oka) load_page<D>(ra, p, ka, pa, g, tp, j);
-  }
+  issue(sa, pg);
   while (pg < pend) {
-    int pn = pg + kWaves;
-    if (pn < pend) {
-      okb = meta(pn, kb, pb);
-      if (okb) load_page<D>(rb, p, kb, pb, g, tp, j);
-    }
-    if (oka) process_page<D, G>(st, ra, p, ka, pa, g, pg, len, tp);
-    else bad = true;
-    pg = pn;
+    issue(sb, pg + kWaves);
+    if (sa.ok) process_page<D, G>(st, sa.r, p, sa.kind, sa.scale, pg, len, tp);
+    pg += kWaves;
     if (pg >= pend) break;
-    pn = pg + kWaves;
-    if (pn < pend) {
-      oka = meta(pn, ka, pa);
-      if (oka) load_page<D>(ra, p, ka, pa, g, tp, j);
-    }
-    if (okb) process_page<D, G>(st, rb, p, kb, pb, g, pg, len, tp);
-    else bad = true;
-    pg = pn;
+    issue(sa, pg + kWaves);
+    if (sb.ok) process_page<D, G>(st, sb.r, p, sb.kind, sb.scale, pg, len, tp);
+    pg += kWaves;
   }
 
   // Merge the 8 token-pair groups of this wavefront (lanes with equal j).
@@ -404,7 +435,8 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeParams p) {
 
 template <int D, int G>
 hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.n_splits, p.num_kv_heads, p.batch);
+  const dim3 grid = kHeadMajorGrid ? dim3(p.num_kv_heads, p.n_splits, p.batch)
+                                   : dim3(p.n_splits, p.num_kv_heads, p.batch);
   if (p.n_splits > 0) {
     if (p.fidelity)
       hipLaunchKernelGGL((decode_splitk_kernel<D, G, true>), grid, dim3(kThreads), 0, stream, p);

@@ -51,6 +51,8 @@ ekv_status check_kv(const ekv_paged_kv* kv, bool need_target, bool need_compact)
   if (!kv) return fail(EKV_ERR_INVALID_ARG, "kv descriptor is NULL");
   if (kv->page_size != EKV_PAGE_SIZE) return fail(EKV_ERR_INVALID_ARG, "page_size %d != %d", kv->page_size, EKV_PAGE_SIZE);
   if (kv->n_target_pages < 0 || kv->n_compact_pages < 0) return fail(EKV_ERR_INVALID_ARG, "negative pool size");
+  if (kv->n_target_pages >= (1 << 30) || kv->n_compact_pages >= (1 << 30))
+    return fail(EKV_ERR_UNSUPPORTED, "pools of 2^30 pages or more are not supported");
   if (need_target || kv->n_target_pages > 0) {
     if (!kv->k_target || !kv->v_target) return fail(EKV_ERR_INVALID_ARG, "target pool pointer is NULL");
     if (!aligned16(kv->k_target) || !aligned16(kv->v_target)) return fail(EKV_ERR_INVALID_ARG, "target pool not 16-byte aligned");
@@ -124,7 +126,7 @@ ekv_status ekv_decode_attention(const ekv_paged_kv* kv, const void* q, int32_t b
     if (has_t == has_c) return fail(EKV_ERR_INVALID_ARG, "fidelity may be NULL only when exactly one pool is non-empty");
     uniform_kind = has_c ? EKV_FIDELITY_COMPACT : EKV_FIDELITY_TARGET;
   }
-  if (pages_per_split < 0 || pages_per_split > 4096) return fail(EKV_ERR_INVALID_ARG, "pages_per_split %d outside 0..4096", pages_per_split);
+  if (pages_per_split < 0 || pages_per_split > 512) return fail(EKV_ERR_INVALID_ARG, "pages_per_split %d outside 0..512", pages_per_split);
   const int32_t pps = pages_per_split > 0 ? pages_per_split
                                           : ekv_decode_pages_per_split(batch, kv->num_kv_heads, max_seq_len);
   const int32_t splits = max_pages > 0 ? ceil_div(max_pages, pps) : 0;

@@ -12,6 +12,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Word 3 of a gfx9 raw buffer descriptor (32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
 
 constexpr int kPage = 16;
 constexpr int kWave = 64;

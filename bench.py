@@ -70,15 +70,16 @@ def main():
     fl = None if args.no_flags else dev(case.fidelity)
     lens = dev(case.seq_lens)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device="cuda")
-    scratch_bytes = ekv.ekv_decode_scratch_bytes(B, Hq, Hkv, D, case.max_seq_len, args.pages_per_split)
+    # split plan from the host-side lengths the scheduler holds
+    pps = args.pages_per_split or ekv.ekv_decode_plan_pages_per_split(case.seq_lens, Hkv)
+    scratch_bytes = ekv.ekv_decode_scratch_bytes(B, Hq, Hkv, D, case.max_seq_len, pps)
     scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device="cuda")
     kvs = [ekv.paged_kv(Hkv, D, k_compact=c["k"], v_compact=c["v"], v_scale=c["s"]) for c in copies]
     stream = torch.cuda.current_stream()
 
     def step(i):
         ekv.ekv_decode_attention(kvs[i % len(kvs)], q, pt, fl, lens, case.max_seq_len, case.sm_scale,
-                                 out, None, scratch, pages_per_split=args.pages_per_split,
-                                 stream=stream)
+                                 out, None, scratch, pages_per_split=pps, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -126,7 +127,7 @@ def main():
                         "page 16, FP16 K + E4M3 V + fp32 page-head scales, 17,408-page pool (seed 2)",
             "batch": B, "context": int(case.seq_lens[0]), "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "page_size": 16, "fidelity_flags_read": fl is not None,
-            "pages_per_split": args.pages_per_split or ekv.ekv_decode_pages_per_split(B, Hkv, case.max_seq_len),
+            "pages_per_split": pps,
             "pool_copies_rotated": len(kvs), "out_dtype": "f16",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -107,6 +107,16 @@ const char* ekv_last_error(void);
 int32_t ekv_decode_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
 
 /*
+ * Decode split plan from HOST-side sequence lengths (int32 [batch], host
+ * memory), for callers whose scheduler knows them: batches of near-equal
+ * lengths get one balanced round of about 512 workgroups; ragged batches get
+ * smaller splits that balance the tail.  Pass the result as
+ * `pages_per_split`.  Pure host function; NULL or empty input returns 16.
+ */
+int32_t ekv_decode_plan_pages_per_split(const int32_t* seq_lens_host, int32_t batch,
+                                        int32_t num_kv_heads);
+
+/*
  * Scratch bytes ekv_decode_attention needs for these sizes (split-K partial
  * results).  `pages_per_split` 0 = the automatic plan.  Pure host function.
  */

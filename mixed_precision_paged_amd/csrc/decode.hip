@@ -44,12 +44,14 @@ constexpr float kTau = 8.0f;          // deferred-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;   // "no token yet" running max
 constexpr bool kHeadMajorGrid = true; // launch order: the KV heads of one (sequence, split) adjacent
 constexpr int kMaxSplitPages = 512;   // pages per split (metadata staged in LDS)
+constexpr int kSlots = 2;             // register page buffers per wavefront (pages in flight + 1)
+constexpr int kMinWaves = 2;          // occupancy bound (wavefronts per SIMD) for G*D < 1024
 
 template <int D>
 struct PageRegs {
-  f16x8 k[D / 32];        // K[token lane%16][32kb + 8(lane/16) .. +8]: MFMA B operand per kb
-  uint32_t v[2][D / 16];  // V rows of tokens tp, tp+8 at this lane's d-set (TARGET fp16;
-                          // COMPACT: the first D/32 dwords hold D/8 E4M3 bytes)
+  f16x8 k[D / 32];       // K[token l%16][32kb + 8(l/16) .. +8]: MFMA A operand of S^T = K Q^T
+  uint32_t v[4][D / 32]; // V rows of tokens 4(l/16)+i at d = (D/16)(l%16) .. +D/16 (fp16 pairs;
+                         // COMPACT: the first D/64 dwords of a row hold its D/16 E4M3 bytes)
 };
 
 // One prefetch slot: a page's K/V registers plus its uniform metadata.
@@ -62,16 +64,16 @@ struct Slot {
 };
 
 // Loads one page's K and V rows of this lane with buffer loads.  The buffer
-// descriptors (wavefront-uniform, SGPRs) cover exactly one page of one KV head,
-// so the hardware range check keeps every access inside that page; `koff`/
-// `voff` are per-lane 32-bit byte offsets (token tp, d-octet j) and the
-// second token's 8-row stride goes in the scalar offset.
+// descriptors (wavefront-uniform, SGPRs) cover exactly one page of one KV
+// head, so the hardware range check keeps every access inside that page.
+// `kqoff` (token l%16, 16 B chunk l/16) and `voff` (token 4(l/16), d chunk
+// l%16) are per-lane byte offsets; the token step of V goes in the scalar
+// offset.  Each V load instruction covers 4 whole token rows.
 template <int D>
 __device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* kbase,
                                           const char* vbase, uint32_t kbytes, uint32_t vbytes,
-                                          uint32_t kqoff, uint32_t koff, uint32_t voff,
-                                          uint32_t krow8, uint32_t vrow8) {
-  constexpr int NC = D / 64;
+                                          uint32_t kqoff, uint32_t voff16, uint32_t voff8,
+                                          uint32_t krow, uint32_t vrow) {
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, kbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, vbytes, kBufferFlags);
 #pragma unroll
@@ -79,143 +81,131 @@ __device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* 
     r.k[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, kqoff + 64u * kb, 0, 0));
   if (kind == 0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vr, koff + 128u * c, t * krow8, 0);
-        r.v[t][4 * c + 0] = y.x; r.v[t][4 * c + 1] = y.y;
-        r.v[t][4 * c + 2] = y.z; r.v[t][4 * c + 3] = y.w;
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (D == 128) {
+        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vr, voff16, i * krow, 0);
+        r.v[i][0] = y.x; r.v[i][1] = y.y; r.v[i][2] = y.z; r.v[i][3] = y.w;
+      } else {
+        const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(vr, voff16, i * krow, 0);
+        r.v[i][0] = y.x; r.v[i][1] = y.y;
       }
+    }
   } else {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 64u * c, t * vrow8, 0);
-        r.v[t][2 * c + 0] = y.x; r.v[t][2 * c + 1] = y.y;
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (D == 128) {
+        const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(vr, voff8, i * vrow, 0);
+        r.v[i][0] = y.x; r.v[i][1] = y.y; r.v[i][2] = 0u; r.v[i][3] = 0u;
+      } else {
+        r.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff8, i * vrow, 0);
+        r.v[i][1] = 0u;
       }
-    // keep every element of the register array defined on both paths (no scratch)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int w = D / 32; w < D / 16; ++w) r.v[t][w] = 0u;
+    }
   }
 }
 
 template <int D, int G>
 struct State {
-  f16x8 qa[D / 32];  // Q[head lane%16][32kb + 8(lane/16) .. +8]: MFMA A operand (0 for head >= G)
-  float m[G], l[G];
-  float acc[G][D / 8];
+  f16x8 qb[D / 32];      // Q[head l%16][32kb + 8(l/16) .. +8]: MFMA B operand (0 for head >= G)
+  float m, l;            // running max (log2 units) and partial sum of head l%16 (this lane's tokens)
+  f32x4 acc[D / 16];     // O[head 4(l/16)+i][d = (D/16)(l%16) + e] in acc[e][i]
 };
+
+__device__ __forceinline__ f16x4 pack4(float a, float b, float c, float d) {
+  return f16x4{(f16)a, (f16)b, (f16)c, (f16)d};
+}
 
 template <int D, int G>
 __device__ __forceinline__ void process_page(State<D, G>& st, PageRegs<D>& r, const DecodeParams& p,
-                                             int kind, float scale, int pg, int len, int tp) {
-  constexpr int DW = D / 16;
+                                             int kind, float scale, int pg, int len, int lane) {
+  constexpr int NE = D / 16;  // PV MFMAs (d columns per lane)
+  const int tq = lane >> 4;
   // Compact scale s = 2^e * f, f in [1, 2): the conversion applies the exact power of two,
   // p carries f.  (Scales are positive normal fp32 values.)
   const uint32_t sbits = kind ? __builtin_bit_cast(uint32_t, scale) : 0x3F800000u;
   const float s_pow2 = as_f32(sbits & 0x7F800000u);
   const float s_frac = as_f32((sbits & 0x807FFFFFu) | 0x3F800000u);
-  const int t0 = pg * kPage + tp;
-  const bool ok0 = t0 < len, ok1 = t0 + 8 < len;
   const bool partial = pg * kPage + kPage > len;  // wavefront-uniform
 
-  // S[h][t] = Q . K^T on the matrix cores: rows = heads (padded to 16), columns = the
-  // page's 16 tokens; lane l receives S[4(l/16)+i][l%16], i < 4.
+  // S^T = K . Q^T on the matrix cores: lane l gets the scores of head l%16 for
+  // tokens 4(l/16)+i of the page (i < 4).
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb)
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.qa[kb], r.k[kb], sacc, 0, 0, 0);
-  // Move the scores of tokens tp and tp+8 to this lane (PV layout).
-  float s0[G], s1[G];
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(r.k[kb], st.qb[kb], sacc, 0, 0, 0);
+  float x[4];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const int src = 16 * (h / 4);
-    const float v = sacc[h % 4];
-    s0[h] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (src + tp), __builtin_bit_cast(int, v))) * p.scale_log2;
-    s1[h] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (src + tp + 8), __builtin_bit_cast(int, v))) * p.scale_log2;
-  }
+  for (int i = 0; i < 4; ++i) x[i] = sacc[i] * p.scale_log2;
   if (partial) {  // last page of the sequence: drop slots >= len (their contents are undefined)
-    const float ninf = -__builtin_inff();
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s0[h] = ok0 ? s0[h] : ninf;
-      s1[h] = ok1 ? s1[h] : ninf;
-    }
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = pg * kPage + 4 * tq + i < len;
+      x[i] = ok ? x[i] : -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < DW; ++w) {
-      r.v[0][w] = ok0 ? r.v[0][w] : 0u;
-      r.v[1][w] = ok1 ? r.v[1][w] : 0u;
+      for (int w = 0; w < D / 32; ++w) r.v[i][w] = ok ? r.v[i][w] : 0u;
     }
   }
 
-  bool raise = false;
-  float mnew[G];
+  // Online softmax per head; the page max spans the 4 lanes holding the head.
+  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
+  const float mnew = (mx > st.m + kTau) ? mx : st.m;
+  if (__ballot(mnew != st.m)) {
+    const float a = fast_exp2(st.m - mnew);  // 1 when unchanged, 0 from kNegBig
+    st.l *= a;
+    // acc rows are heads 4(l/16)+i: fetch their factors from lanes 4(l/16)+i
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mx = fmaxf(s0[h], s1[h]);
-    mnew[h] = (mx > st.m[h] + kTau) ? mx : st.m[h];
-    raise |= mnew[h] != st.m[h];
-  }
-  if (__ballot(raise)) {
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (4 * tq + i), __builtin_bit_cast(int, a)));
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float a = fast_exp2(st.m[h] - mnew[h]);  // 1 when unchanged, 0 from kNegBig
-      st.l[h] *= a;
-#pragma unroll
-      for (int e = 0; e < D / 8; ++e) st.acc[h][e] *= a;
-      st.m[h] = mnew[h];
+      for (int e = 0; e < NE; ++e) st.acc[e][i] *= ai;
     }
+    st.m = mnew;
   }
-
-  float pf[G][2];  // fp32 probabilities of the lane's two tokens (times f on compact pages)
+  float pv[4];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float p0 = fast_exp2(s0[h] - st.m[h]);
-    const float p1 = fast_exp2(s1[h] - st.m[h]);
-    st.l[h] += p0 + p1;
-    pf[h][0] = p0 * s_frac;
-    pf[h][1] = p1 * s_frac;
+  for (int i = 0; i < 4; ++i) {
+    pv[i] = fast_exp2(x[i] - st.m);
+    st.l += pv[i];
+    pv[i] *= s_frac;
   }
+  // P (A operand of the 16x16x16 P.V MFMA) in two fp16 parts: p = hi + lo to ~22 bits.
+  const f16x4 phi = pack4(pv[0], pv[1], pv[2], pv[3]);
+  const f16x4 plo = pack4(pv[0] - (float)phi[0], pv[1] - (float)phi[1], pv[2] - (float)phi[2],
+                          pv[3] - (float)phi[3]);
 
-  // PV with fp32 p and fp32 accumulation; the fp16 value operand is exact
-  // (v_fma_mix_f32 reads either half of a packed fp16 register).
+  // V operands: for column set e, lane l holds V[tokens 4(l/16)..+3][d = (D/16)(l%16) + e].
+  f16x4 vb[NE];
   if (kind == 0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int w = 0; w < DW; ++w) {
-        const f16x2 v = as_f16x2(r.v[t][w]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          st.acc[h][2 * w] = __builtin_fmaf((float)v.x, pf[h][t], st.acc[h][2 * w]);
-          st.acc[h][2 * w + 1] = __builtin_fmaf((float)v.y, pf[h][t], st.acc[h][2 * w + 1]);
-        }
-      }
+    for (int w = 0; w < NE / 2; ++w) {
+      const uint32_t e0 = perm(r.v[1][w], r.v[0][w], 0x05040100u), e1 = perm(r.v[3][w], r.v[2][w], 0x05040100u);
+      const uint32_t o0 = perm(r.v[1][w], r.v[0][w], 0x07060302u), o1 = perm(r.v[3][w], r.v[2][w], 0x07060302u);
+      vb[2 * w] = __builtin_bit_cast(f16x4, u32x2{e0, e1});
+      vb[2 * w + 1] = __builtin_bit_cast(f16x4, u32x2{o0, o1});
+    }
   } else {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int w = 0; w < NE / 4; ++w) {
+      const uint32_t a01 = perm(r.v[1][w], r.v[0][w], 0x05010400u), a23 = perm(r.v[3][w], r.v[2][w], 0x05010400u);
+      const uint32_t b01 = perm(r.v[1][w], r.v[0][w], 0x07030602u), b23 = perm(r.v[3][w], r.v[2][w], 0x07030602u);
+      vb[4 * w + 0] = __builtin_bit_cast(f16x4, u32x2{bits(e4m3x2_scaled_f16(a01, s_pow2, false)), bits(e4m3x2_scaled_f16(a23, s_pow2, false))});
+      vb[4 * w + 1] = __builtin_bit_cast(f16x4, u32x2{bits(e4m3x2_scaled_f16(a01, s_pow2, true)), bits(e4m3x2_scaled_f16(a23, s_pow2, true))});
+      vb[4 * w + 2] = __builtin_bit_cast(f16x4, u32x2{bits(e4m3x2_scaled_f16(b01, s_pow2, false)), bits(e4m3x2_scaled_f16(b23, s_pow2, false))});
+      vb[4 * w + 3] = __builtin_bit_cast(f16x4, u32x2{bits(e4m3x2_scaled_f16(b01, s_pow2, true)), bits(e4m3x2_scaled_f16(b23, s_pow2, true))});
+    }
+  }
 #pragma unroll
-      for (int w = 0; w < DW / 2; ++w) {
-        const f16x2 lo = e4m3x2_scaled_f16(r.v[t][w], s_pow2, false);  // d = 4w, 4w+1
-        const f16x2 hi = e4m3x2_scaled_f16(r.v[t][w], s_pow2, true);   // d = 4w+2, 4w+3
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          st.acc[h][4 * w + 0] = __builtin_fmaf((float)lo.x, pf[h][t], st.acc[h][4 * w + 0]);
-          st.acc[h][4 * w + 1] = __builtin_fmaf((float)lo.y, pf[h][t], st.acc[h][4 * w + 1]);
-          st.acc[h][4 * w + 2] = __builtin_fmaf((float)hi.x, pf[h][t], st.acc[h][4 * w + 2]);
-          st.acc[h][4 * w + 3] = __builtin_fmaf((float)hi.y, pf[h][t], st.acc[h][4 * w + 3]);
-        }
-      }
+  for (int e = 0; e < NE; ++e) {
+    st.acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(phi, vb[e], st.acc[e], 0, 0, 0);
+    st.acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(plo, vb[e], st.acc[e], 0, 0, 0);
   }
 }
 
 template <int D, int G, bool FLAGS>
-__global__ __launch_bounds__(kThreads, (G * D >= 1024 ? 1 : 2)) void decode_splitk_kernel(DecodeParams p) {
-  constexpr int NC = D / 64;
-  constexpr int DE = D / 8;
+__global__ __launch_bounds__(kThreads, kMinWaves) void decode_splitk_kernel(DecodeParams p) {
+  constexpr int NE = D / 16;
   __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
@@ -225,7 +215,6 @@ __global__ __launch_bounds__(kThreads, (G * D >= 1024 ? 1 : 2)) void decode_spli
   const int lane = threadIdx.x & (kWave - 1);
   // wavefront index made provably uniform, so page metadata becomes scalar loads
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int j = lane & 7, tp = lane >> 3;
   const int split = kHeadMajorGrid ? blockIdx.y : blockIdx.x;
   const int g = kHeadMajorGrid ? blockIdx.x : blockIdx.y;
   const int b = blockIdx.z;
@@ -238,18 +227,15 @@ __global__ __launch_bounds__(kThreads, (G * D >= 1024 ? 1 : 2)) void decode_spli
   State<D, G> st;
   {
     const int qh = lane & 15, qc = lane >> 4;
-    const uint16_t* qp = p.q + ((int64_t)b * p.num_q_heads + g * G + qh) * D + 8 * qc;
+    const uint16_t* qp = p.q + ((int64_t)b * p.num_q_heads + g * G + (qh < G ? qh : 0)) * D + 8 * qc;
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb)
-      st.qa[kb] = qh < G ? __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(qp + 32 * kb)) : f16x8{};
+      st.qb[kb] = qh < G ? __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(qp + 32 * kb)) : f16x8{};
   }
+  st.m = kNegBig;
+  st.l = 0.f;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    st.m[h] = kNegBig;
-    st.l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < DE; ++e) st.acc[h][e] = 0.f;
-  }
+  for (int e = 0; e < NE; ++e) st.acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Stage this split's page metadata in LDS once: (phys << 1 | kind), or -1
   // for an out-of-range id or unknown flag.  Per-page reads are then LDS
@@ -267,12 +253,12 @@ __global__ __launch_bounds__(kThreads, (G * D >= 1024 ? 1 : 2)) void decode_spli
   }
   __syncthreads();
 
-  // Per-lane byte offsets inside a page (token tp, d-octet j) and 8-row strides.
+  // Per-lane byte offsets inside a page.
   const uint32_t krow = (uint32_t)p.num_kv_heads * D * 2u;   // bytes per token row, fp16
   const uint32_t vrow = (uint32_t)p.num_kv_heads * D;        // bytes per token row, E4M3
-  const uint32_t koff = (uint32_t)tp * krow + 16u * j;          // V16 rows (PV layout)
-  const uint32_t kqoff = (uint32_t)(lane & 15) * krow + 16u * (lane >> 4);  // K rows (MFMA layout)
-  const uint32_t voff = (uint32_t)tp * vrow + 8u * j;
+  const uint32_t kqoff = (uint32_t)(lane & 15) * krow + 16u * (lane >> 4);      // K: token l%16
+  const uint32_t voff16 = 4u * (lane >> 4) * krow + (uint32_t)(lane & 15) * (D / 8);  // V16: tokens 4(l/16)+i
+  const uint32_t voff8 = 4u * (lane >> 4) * vrow + (uint32_t)(lane & 15) * (D / 16);  // V8
   const int64_t kpage = (int64_t)kPage * krow, vpage8 = (int64_t)kPage * vrow;
   bool bad = false;
 
@@ -291,59 +277,60 @@ __global__ __launch_bounds__(kThreads, (G * D >= 1024 ? 1 : 2)) void decode_spli
     const uint32_t kbytes = (uint32_t)kpage - (uint32_t)g * D * 2;
     const uint32_t vbytes = sl.kind ? (uint32_t)vpage8 - (uint32_t)g * D : kbytes;
     sl.scale = sl.kind ? p.v_scale[(int64_t)phys * p.num_kv_heads + g] : 1.0f;
-    load_page<D>(sl.r, sl.kind, kb, vb, kbytes, vbytes, kqoff, koff, voff, 8u * krow, 8u * vrow);
+    load_page<D>(sl.r, sl.kind, kb, vb, kbytes, vbytes, kqoff, voff16, voff8, krow, vrow);
   };
-  // Two slots: page pg+4 loads while page pg computes.
-  Slot<D> sa, sb;
+  // kSlots register page buffers: pages pg+4 .. pg+4(kSlots-1) load while page pg
+  // computes.  Slots are named variables (never an indexed array) so they stay
+  // in registers.
+  static_assert(kSlots >= 2 && kSlots <= 6, "kSlots in 2..6");
   int pg = pbeg + wave;
-  issue(sa, pg);
+  Slot<D> s0, s1, s2, s3, s4, s5;
+#define EKV_STEP(CUR, NXT)                                                        \
+  issue(NXT, pg + (kSlots - 1) * kWaves);                                         \
+  if (CUR.ok) process_page<D, G>(st, CUR.r, p, CUR.kind, CUR.scale, pg, len, lane); \
+  pg += kWaves;                                                                   \
+  if (pg >= pend) break;
+  issue(s0, pg);
+  if (kSlots > 2) issue(s1, pg + kWaves);
+  if (kSlots > 3) issue(s2, pg + 2 * kWaves);
+  if (kSlots > 4) issue(s3, pg + 3 * kWaves);
+  if (kSlots > 5) issue(s4, pg + 4 * kWaves);
   while (pg < pend) {
-    issue(sb, pg + kWaves);
-    if (sa.ok) process_page<D, G>(st, sa.r, p, sa.kind, sa.scale, pg, len, tp);
-    pg += kWaves;
-    if (pg >= pend) break;
-    issue(sa, pg + kWaves);
-    if (sb.ok) process_page<D, G>(st, sb.r, p, sb.kind, sb.scale, pg, len, tp);
-    pg += kWaves;
+    if constexpr (kSlots == 2) {
+      EKV_STEP(s0, s1) EKV_STEP(s1, s0)
+    } else if constexpr (kSlots == 3) {
+      EKV_STEP(s0, s2) EKV_STEP(s1, s0) EKV_STEP(s2, s1)
+    } else if constexpr (kSlots == 4) {
+      EKV_STEP(s0, s3) EKV_STEP(s1, s0) EKV_STEP(s2, s1) EKV_STEP(s3, s2)
+    } else if constexpr (kSlots == 5) {
+      EKV_STEP(s0, s4) EKV_STEP(s1, s0) EKV_STEP(s2, s1) EKV_STEP(s3, s2) EKV_STEP(s4, s3)
+    } else {
+      EKV_STEP(s0, s5) EKV_STEP(s1, s0) EKV_STEP(s2, s1) EKV_STEP(s3, s2) EKV_STEP(s4, s3)
+      EKV_STEP(s5, s4)
+    }
   }
+#undef EKV_STEP
 
-  // Merge the 8 token-pair groups of this wavefront (lanes with equal j).
+  // This wavefront's totals: head h's sum spans lanes h, h+16, h+32, h+48;
+  // its output rows are acc[e][i] for h = 4(l/16)+i, d = (D/16)(l%16) + e.
+  float L = st.l + shfl_xor(st.l, 16);
+  L += shfl_xor(L, 32);
+  {
+    const int tq = lane >> 4, dq = lane & 15;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float M = st.m[h];
-    M = fmaxf(M, dpp<kDppRowRor8>(M));
-    M = fmaxf(M, shfl_xor(M, 16));
-    M = fmaxf(M, shfl_xor(M, 32));
-    const float f = fast_exp2(st.m[h] - M);
-    float L = st.l[h] * f;
-    L += dpp<kDppRowRor8>(L);
-    L += shfl_xor(L, 16);
-    L += shfl_xor(L, 32);
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * tq + i;
+      if (h < G) {
 #pragma unroll
-    for (int e = 0; e < DE; ++e) {
-      float a = st.acc[h][e] * f;
-      a += dpp<kDppRowRor8>(a);
-      a += shfl_xor(a, 16);
-      a += shfl_xor(a, 32);
-      st.acc[h][e] = a;
+        for (int e = 0; e < NE; ++e) s_acc[wave][h][NE * dq + e] = st.acc[e][i];
+      }
     }
-    st.m[h] = M;
-    st.l[h] = L;
-  }
-  if (tp == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < DE; ++e) s_acc[wave][h][64 * (e / 8) + 8 * j + (e % 8)] = st.acc[h][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s_m[wave][h] = st.m[h];
-      s_l[wave][h] = st.l[h];
+    if (tq == 0 && dq < G) {
+      s_m[wave][dq] = st.m;
+      s_l[wave][dq] = L;
     }
-    s_bad[wave] = bad ? 1 : 0;
   }
+  if (lane == 0) s_bad[wave] = bad ? 1 : 0;
   __syncthreads();
 
   // Merge the wavefronts and write this split's partial result.
@@ -464,11 +451,14 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 int32_t decode_auto_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages) {
+  // About 512 workgroups (two 4-wavefront groups per CU) if every sequence had
+  // max_pages pages: measured best on the 256-CU part; splits are whole
+  // multiples of the 4 wavefronts' page stride, between 16 and 512 pages.
   if (max_pages <= 0) return 16;
   const int64_t seqs = (int64_t)batch * num_kv_heads;
-  int32_t c = 512;
-  while (c > 16 && seqs * ((max_pages + c - 1) / c) < 2048) c /= 2;
-  return c;
+  int64_t c = (seqs * max_pages + 511) / 512;
+  c = (c + 3) / 4 * 4;
+  return (int32_t)(c < 16 ? 16 : (c > 512 ? 512 : c));
 }
 
 size_t decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

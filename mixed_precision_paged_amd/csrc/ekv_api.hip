@@ -91,6 +91,24 @@ int32_t ekv_decode_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t 
   return ekv::decode_auto_pages_per_split(batch, num_kv_heads, ceil_div(max_seq_len, EKV_PAGE_SIZE));
 }
 
+int32_t ekv_decode_plan_pages_per_split(const int32_t* seq_lens_host, int32_t batch,
+                                        int32_t num_kv_heads) {
+  if (!seq_lens_host || batch <= 0 || num_kv_heads <= 0) return 16;
+  int64_t total = 0, maxp = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = seq_lens_host[b] > 0 ? (seq_lens_host[b] + EKV_PAGE_SIZE - 1) / EKV_PAGE_SIZE : 0;
+    total += n;
+    maxp = n > maxp ? n : maxp;
+  }
+  if (maxp == 0) return 16;
+  if (total * 10 >= maxp * batch * 9)  // lengths within ~10% of the longest: one balanced round
+    return ekv::decode_auto_pages_per_split(batch, num_kv_heads, (int32_t)maxp);
+  // ragged lengths: small splits (about 4096 of them over all KV heads) balance the tail
+  int64_t c = (total * num_kv_heads + 4095) / 4096;
+  c = (c + 3) / 4 * 4;
+  return (int32_t)(c < 16 ? 16 : (c > 512 ? 512 : c));
+}
+
 size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_seq_len, int32_t pages_per_split) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;

@@ -35,6 +35,7 @@ EKV_F32 = 1
 
 EXPORTED = (
     "ekv_abi_version", "ekv_status_string", "ekv_last_error", "ekv_decode_pages_per_split",
+    "ekv_decode_plan_pages_per_split",
     "ekv_decode_scratch_bytes", "ekv_decode_attention", "ekv_gather_compact_pages",
     "ekv_prefill_attention", "ekv_e4m3_to_f16",
 )
@@ -56,6 +57,8 @@ _lib.ekv_status_string.argtypes = [ctypes.c_int]
 _lib.ekv_last_error.restype = ctypes.c_char_p
 _lib.ekv_decode_pages_per_split.restype = _i32
 _lib.ekv_decode_pages_per_split.argtypes = [_i32, _i32, _i32]
+_lib.ekv_decode_plan_pages_per_split.restype = _i32
+_lib.ekv_decode_plan_pages_per_split.argtypes = [_vp, _i32, _i32]
 _lib.ekv_decode_scratch_bytes.restype = _sz
 _lib.ekv_decode_scratch_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 _lib.ekv_decode_attention.restype = ctypes.c_int
@@ -132,6 +135,15 @@ def paged_kv(num_kv_heads: int, head_dim: int, k_target=None, v_target=None, k_c
 
 def ekv_decode_pages_per_split(batch: int, num_kv_heads: int, max_seq_len: int) -> int:
     return int(_lib.ekv_decode_pages_per_split(batch, num_kv_heads, max_seq_len))
+
+
+def ekv_decode_plan_pages_per_split(seq_lens_host, num_kv_heads: int) -> int:
+    """Split plan from host-side lengths (a numpy int32 array or sequence)."""
+    import numpy as np
+
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    return int(_lib.ekv_decode_plan_pages_per_split(lens.ctypes.data if lens.size else None,
+                                                    int(lens.size), int(num_kv_heads)))
 
 
 def ekv_decode_scratch_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

@@ -22,7 +22,7 @@ def _declared():
 
 def test_every_declared_function_is_exported():
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(ekv._lib, n), n
     assert sorted(ekv.EXPORTED) == names
@@ -90,6 +90,18 @@ def test_split_plan_and_scratch_size():
     assert ekv.ekv_decode_scratch_bytes(32, 32, 8, 128, 8192, 0) == expect
     assert ekv.ekv_decode_scratch_bytes(2, 4, 1, 64, 64, 1) == ((2 * 4 * 4 * 64 * 4 + 255) // 256) * 256 + 2 * 4 * 4 * 8
     assert ekv.ekv_decode_scratch_bytes(0, 4, 1, 64, 64, 1) == 0
+
+
+def test_split_plan_from_host_lengths():
+    import numpy as np
+    uniform = ekv.ekv_decode_plan_pages_per_split(np.full(32, 8192), 8)
+    assert uniform == ekv.ekv_decode_pages_per_split(32, 8, 8192) == 256
+    lens = np.random.default_rng(0).integers(1024, 16385, size=64)
+    ragged = ekv.ekv_decode_plan_pages_per_split(lens, 8)
+    pages = int(((lens + 15) // 16).sum())
+    assert ragged % 4 == 0 and 16 <= ragged <= 512 and abs(ragged - pages * 8 / 4096) <= 4
+    assert ekv.ekv_decode_plan_pages_per_split([], 8) == 16
+    assert ekv.ekv_decode_plan_pages_per_split([0, 0], 8) == 16
 
 
 def test_gather_validation():

@@ -41,11 +41,28 @@ def parse():
     ap.add_argument("--no-flags", action="store_true", help="single-pool path (no per-page flag reads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for 1 GiB in, 1 GiB out."""
+    import torch
+
+    src = torch.ones(1 << 29, dtype=torch.float16, device="cuda")  # 1 GiB
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30}))
 
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the decode hot path on a single MI355X "
               "(sequences and KV heads shard across GPUs with no exchange; not built here).",
@@ -140,13 +157,31 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": counted_traffic() if (fl is not None and pps == 256) else None,
             "avg_call_us": round(kernel_ms * 1e3, 2),
         },
         "cpu_baseline": cpu,
         "input_generation_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def counted_traffic():
+    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when the decode kernel sources changed since it was taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", "decode_compact_b32_ctx8192_pmc.md")
+    srcs = [os.path.join(ROOT, "mixed_precision_paged_amd", "csrc", f)
+            for f in ("decode.hip", "ekv_device.hpp", "ekv_internal.hpp")]
+    try:
+        text = open(path).read()
+        rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
+        h = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()
+    except (OSError, AttributeError, ValueError):
+        return None
+    return int(rec["traffic_bytes_per_call"]) if rec.get("kernel_sources_sha256") == h else None
 
 
 def cpu_baseline(case, algo_bytes, min_seconds):

@@ -1,0 +1,132 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+
+Decode: every output element against the oracle.  Gather: bit-exact on a full
+4,096-page chunk.  Prefill: sampled rows (tile boundaries, first/last rows,
+random rows) per prompt, every head, against the oracle row by row.  Mixed
+batch: one layer routed into one output tensor, decode rows fully checked,
+prefill rows sampled, and every row written by exactly its own path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (DeviceCase, assert_close, assert_lse_close, dev, ekv, max_abs,
+                         oracle_decode, step)
+from mixed_precision_paged_amd import synth
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+SAMPLE_ROWS = (0, 1, 15, 16, 63, 64, 127, 128, 129, 2047, 4095, 4096, 8190, 8191)
+
+
+def _decode_full(case):
+    dc = DeviceCase(case)
+    pps = ekv().ekv_decode_plan_pages_per_split(case.seq_lens, case.num_kv_heads)
+    out, lse = dc.decode(torch.float32, pages_per_split=pps)
+    want, wlse = oracle_decode(case)
+    assert_close(out, want)
+    assert_lse_close(lse, wlse)
+    return out
+
+
+def test_compact_decode_b32_ctx8192():
+    step("fullsize compact decode B=32 ctx 8192")
+    _decode_full(synth.compact_decode_case(seed=2))
+
+
+def test_mixed_decode_b64_ragged_with_outliers():
+    step("fullsize mixed decode B=64 ctx U[1024,16384], 30% compact, 1% x20 outliers")
+    c = synth.mixed_decode_case(seed=3)
+    _decode_full(c)
+
+
+def _sample_rows(L, rng, extra=6):
+    rows = [r for r in SAMPLE_ROWS if r < L]
+    rows += list(rng.choice(L, size=min(extra, L), replace=False))
+    return sorted(set(int(r) for r in rows))
+
+
+def test_compact_prefill_32x8192_in_four_chunks():
+    step("fullsize compact prefill 32 x 8192, 4 chunks of 4096 pages")
+    pc = synth.compact_prefill_case(seed=4)
+    c = pc.paged
+    dc = DeviceCase(c)
+    H, D, Hq = c.num_kv_heads, c.head_dim, c.num_q_heads
+    ws_k = torch.empty((4096, 16, H, D), dtype=torch.float16, device="cuda")
+    ws_v = torch.empty_like(ws_k)
+    rng = np.random.default_rng(44)
+    for chunk in range(4):
+        prompts = list(range(8 * chunk, 8 * chunk + 8))
+        ids, kv_start = pc.chunk_pages(prompts)
+        assert ids.size == 4096
+        step(f"chunk {chunk}: gather 4096 pages")
+        ekv().ekv_gather_compact_pages(dc.kv(), dev(ids), True, ws_k, ws_v)
+        rows = np.arange(pc.cu_seqlens_q[prompts[0]], pc.cu_seqlens_q[prompts[-1] + 1])
+        q = dev(c.q[rows])
+        cu = (pc.cu_seqlens_q[prompts[0]:prompts[-1] + 2] - pc.cu_seqlens_q[prompts[0]]).astype(np.int32)
+        out = torch.empty((rows.size, Hq, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((rows.size, Hq), dtype=torch.float32, device="cuda")
+        step(f"chunk {chunk}: prefill 8 x 8192")
+        ekv().ekv_prefill_attention(q, ws_k, ws_v, dev(cu), dev(kv_start), 8192, c.sm_scale, out, lse)
+        torch.cuda.synchronize()
+        wk, wv = oracle.gather_compact_pages(c.k_compact, c.v_compact, c.v_scale, ids, True)
+        if chunk == 0:  # bit-exact gather over the whole workspace
+            gk, gv = ws_k.cpu().numpy(), ws_v.cpu().numpy()
+            assert np.array_equal(gk.view(np.uint16), wk.view(np.uint16))
+            assert np.array_equal(gv.view(np.uint16), wv.view(np.uint16))
+        sample = []
+        for i, pidx in enumerate(prompts):
+            sample += [int(cu[i]) + r for r in _sample_rows(8192, rng)]
+        sample = np.array(sample)
+        got = out[dev(sample).long()].cpu().numpy()
+        glse = lse[dev(sample).long()].cpu().numpy()
+        want, wlse = oracle.prefill_attention(c.q[rows], wk.reshape(-1, H, D), wv.reshape(-1, H, D),
+                                              cu, kv_start, True, c.sm_scale, rows=sample)
+        assert_close(got, want[sample], what=f"chunk {chunk} prefill rows")
+        assert_lse_close(glse, wlse[sample])
+        del out, lse, q
+
+
+def test_mixed_batch_one_layer_routed():
+    """Decode rows 0..31 and prefill rows 32.. of one layer land in one output tensor."""
+    step("fullsize mixed batch layer 0: gather -> prefill -> decode")
+    L = synth.mixed_batch_layer(0)
+    c = L.paged
+    dc = DeviceCase(c)
+    H, D, Hq = c.num_kv_heads, c.head_dim, c.num_q_heads
+    nd = L.n_decode
+    T = int(L.cu_seqlens_q[-1])
+    out = torch.full((nd + T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((nd + T, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    # prefill route first (workspace reused per layer), then decode
+    prompts = list(range(nd, nd + len(L.prompt_lens)))
+    ids = np.concatenate([c.page_table[p, :(int(c.seq_lens[p]) + 15) // 16] for p in prompts]).astype(np.int32)
+    kv_start = np.concatenate([[0], np.cumsum((L.prompt_lens + 15) // 16 * 16)[:-1]]).astype(np.int32)
+    ws_k = torch.empty((4096, 16, H, D), dtype=torch.float16, device="cuda")
+    ws_v = torch.empty_like(ws_k)
+    ekv().ekv_gather_compact_pages(dc.kv(), dev(ids), True, ws_k, ws_v)
+    ekv().ekv_prefill_attention(dev(L.q_prefill), ws_k, ws_v, dev(L.cu_seqlens_q), dev(kv_start),
+                                int(L.prompt_lens.max()), c.sm_scale, out[nd:], lse[nd:])
+    lens = c.seq_lens[:nd]
+    pps = ekv().ekv_decode_plan_pages_per_split(lens, H)
+    ekv().ekv_decode_attention(dc.kv(), dev(L.q_decode), dc.page_table[:nd].contiguous(),
+                               dc.fidelity[:nd].contiguous(), dev(lens), int(lens.max()), c.sm_scale,
+                               out[:nd], lse[:nd], pages_per_split=pps)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    ls = lse.cpu().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ls)), "every row written by its own path"
+    want, wlse = oracle.decode_attention(L.q_decode, c.k_target, c.v_target, c.k_compact, c.v_compact,
+                                         c.v_scale, c.page_table[:nd], c.fidelity[:nd], lens, c.sm_scale)
+    assert_close(o[:nd], want, what="decode rows")
+    assert_lse_close(ls[:nd], wlse)
+    wk, wv = oracle.gather_compact_pages(c.k_compact, c.v_compact, c.v_scale, ids, True)
+    rng = np.random.default_rng(5)
+    sample = []
+    for i in range(len(prompts)):
+        sample += [int(L.cu_seqlens_q[i]) + r for r in _sample_rows(int(L.prompt_lens[i]), rng)]
+    pw, plw = oracle.prefill_attention(L.q_prefill, wk.reshape(-1, H, D), wv.reshape(-1, H, D),
+                                       L.cu_seqlens_q, kv_start, True, c.sm_scale, rows=sample)
+    assert_close(o[nd:][sample], pw[sample], what="prefill rows")
+    assert_lse_close(ls[nd:][sample], plw[sample])

@@ -41,6 +41,12 @@ def parse():
     ap.add_argument("--no-flags", action="store_true", help="single-pool path (no per-page flag reads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time")
+    ap.add_argument("--workload", choices=("decode", "prefill", "mixed"), default="decode",
+                    help="decode: the headline line; prefill: 32 x 8192 compact-prefill route "
+                         "(gather + causal prefill, 4 chunks); mixed: the 36-layer mixed batch")
+    ap.add_argument("--layers", type=int, default=36, help="mixed workload: layers per step")
+    ap.add_argument("--distinct-layers", type=int, default=4,
+                    help="mixed workload: distinct generated layers cycled over the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -62,6 +68,12 @@ def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.workload == "prefill":
+        bench_prefill(args)
+        return
+    if args.workload == "mixed":
+        bench_mixed(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the decode hot path on a single MI355X "
@@ -162,6 +174,156 @@ def main():
         },
         "cpu_baseline": cpu,
         "input_generation_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+MFMA_FP16_PEAK_TFLOPS = 2500.0
+
+
+def _events(n):
+    import torch
+
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def bench_prefill(args):
+    """Compact-prefill route, 32 fresh prompts x 8192 tokens: per 4,096-page chunk of 8
+    prompts, gather (K copy + E4M3 -> FP16 with scales) then causal FP16 prefill."""
+    import torch
+
+    from mixed_precision_paged_amd import bytemodel, ekv, synth
+
+    pc = synth.compact_prefill_case(seed=4)
+    c = pc.paged
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    H, D, Hq = c.num_kv_heads, c.head_dim, c.num_q_heads
+    kv = ekv.paged_kv(H, D, k_compact=dev(c.k_compact), v_compact=dev(c.v_compact), v_scale=dev(c.v_scale))
+    q = dev(c.q)
+    out = torch.empty((q.shape[0], Hq, D), dtype=torch.float16, device="cuda")
+    ws_k = torch.empty((4096, 16, H, D), dtype=torch.float16, device="cuda")
+    ws_v = torch.empty_like(ws_k)
+    chunks = []
+    for ch in range(4):
+        prompts = list(range(8 * ch, 8 * ch + 8))
+        ids, kv_start = pc.chunk_pages(prompts)
+        r0, r1 = int(pc.cu_seqlens_q[prompts[0]]), int(pc.cu_seqlens_q[prompts[-1] + 1])
+        cu = (pc.cu_seqlens_q[prompts[0]:prompts[-1] + 2] - r0).astype(np.int32)
+        chunks.append((dev(ids), dev(kv_start), dev(cu), r0, r1))
+    stream = torch.cuda.current_stream()
+
+    def run(evg=None, evp=None):
+        for i, (ids, ks, cu, r0, r1) in enumerate(chunks):
+            if evg: evg[i][0].record(stream)
+            ekv.ekv_gather_compact_pages(kv, ids, True, ws_k, ws_v, stream=stream)
+            if evg: evg[i][1].record(stream)
+            if evp: evp[i][0].record(stream)
+            ekv.ekv_prefill_attention(q[r0:r1], ws_k, ws_v, cu, ks, 8192, c.sm_scale, out[r0:r1],
+                                      stream=stream)
+            if evp: evp[i][1].record(stream)
+
+    for _ in range(max(1, args.warmup // 2)):
+        run()
+    torch.cuda.synchronize()
+    steps = max(1, min(args.steps, 10))
+    g_ms, p_ms = [], []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        evg, evp = _events(4), _events(4)
+        run(evg, evp)
+        torch.cuda.synchronize()
+        g_ms += [a.elapsed_time(b) for a, b in evg]
+        p_ms += [a.elapsed_time(b) for a, b in evp]
+    wall = (time.perf_counter() - t0) / steps
+    rd, wr = bytemodel.gather_bytes(4096, H, D)
+    flops = bytemodel.prefill_flops([8192] * 8, Hq, D, causal=True)
+    g = float(np.mean(g_ms)) * 1e-3
+    p = float(np.mean(p_ms)) * 1e-3
+    line = {
+        "metric": "compact-prefill route: gather HBM GB/s + causal prefill TFLOP/s",
+        "value": round(flops / p / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "ms_per_step": round(wall * 1e3, 3), "higher_is_better": True, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "compact prefill: 32 fresh prompts x 8192 tokens, 32 q / 8 KV heads, "
+                               "head dim 128, causal, 4,096-page workspace, 4 chunks of 8 prompts (seed 4)"},
+        "prefill": {"avg_chunk_ms": round(p * 1e3, 3), "flops_per_chunk": flops,
+                    "tflops": round(flops / p / 1e12, 1), "peak_tflops": MFMA_FP16_PEAK_TFLOPS,
+                    "mfma_frac": round(flops / p / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4)},
+        "gather": {"avg_chunk_us": round(g * 1e6, 1), "bytes_per_chunk": rd + wr,
+                   "gbps": round((rd + wr) / g / 1e9, 1), "peak_gbps": HBM_PEAK_GBPS,
+                   "frac": round((rd + wr) / g / 1e9 / HBM_PEAK_GBPS, 4)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_mixed(args):
+    """Mixed batch: per layer, gather the 4 fresh prompts' pages, causal prefill (rows 32..),
+    then mixed-fidelity decode of the 32 running sequences (rows 0..31), one stream."""
+    import torch
+
+    from mixed_precision_paged_amd import bytemodel, ekv, synth
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    layers = []
+    for li in range(max(1, args.distinct_layers)):
+        L = synth.mixed_batch_layer(li)
+        c = L.paged
+        H, D, Hq, nd = c.num_kv_heads, c.head_dim, c.num_q_heads, L.n_decode
+        prompts = range(nd, nd + len(L.prompt_lens))
+        ids = np.concatenate([c.page_table[p, :(int(c.seq_lens[p]) + 15) // 16] for p in prompts]).astype(np.int32)
+        ks = np.concatenate([[0], np.cumsum((L.prompt_lens + 15) // 16 * 16)[:-1]]).astype(np.int32)
+        lens = c.seq_lens[:nd]
+        layers.append(dict(
+            kv=ekv.paged_kv(H, D, dev(c.k_target), dev(c.v_target), dev(c.k_compact), dev(c.v_compact),
+                            dev(c.v_scale)),
+            q=dev(np.concatenate([L.q_decode, L.q_prefill])), ids=dev(ids), ks=dev(ks),
+            cu=dev(L.cu_seqlens_q), pt=dev(c.page_table[:nd]), fl=dev(c.fidelity[:nd]), lens=dev(lens),
+            max_len=int(lens.max()), pps=ekv.ekv_decode_plan_pages_per_split(lens, H),
+            dec_bytes=bytemodel.decode_bytes(lens, c.fidelity[:nd], Hq, H, D, out_bytes=2),
+            flops=bytemodel.prefill_flops(L.prompt_lens, Hq, D), sm=c.sm_scale,
+            plen=int(L.prompt_lens.max())))
+        del L, c
+    H, D, Hq, nd = 8, 128, 32, 32
+    T = layers[0]["q"].shape[0]
+    out = torch.empty((T, Hq, D), dtype=torch.float16, device="cuda")
+    ws_k = torch.empty((4096, 16, H, D), dtype=torch.float16, device="cuda")
+    ws_v = torch.empty_like(ws_k)
+    scratch = torch.empty(max(ekv.ekv_decode_scratch_bytes(nd, Hq, H, D, l["max_len"], l["pps"])
+                              for l in layers), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for li in range(args.layers):
+            l = layers[li % len(layers)]
+            ekv.ekv_gather_compact_pages(l["kv"], l["ids"], True, ws_k, ws_v, stream=stream)
+            ekv.ekv_prefill_attention(l["q"][nd:], ws_k, ws_v, l["cu"], l["ks"], l["plen"], l["sm"],
+                                      out[nd:], stream=stream)
+            ekv.ekv_decode_attention(l["kv"], l["q"][:nd], l["pt"], l["fl"], l["lens"], l["max_len"],
+                                     l["sm"], out[:nd], None, scratch, pages_per_split=l["pps"],
+                                     stream=stream)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    steps = max(1, min(args.steps, 20))
+    e0, e1 = _events(1)[0]
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    dec_bytes = sum(layers[li % len(layers)]["dec_bytes"] for li in range(args.layers))
+    line = {
+        "metric": "mixed batch step time (36 layers: gather + prefill + mixed-fidelity decode)",
+        "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": steps, "higher_is_better": False,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"mixed batch: {args.layers} layers ({len(layers)} distinct seeded layers "
+                               "cycled), 32 decoding requests ctx U[4096,32768] 30% compact pages + 4 fresh "
+                               "prompts x 2048 on the gather+prefill route, 32 q / 8 KV heads, head dim 128"},
+        "tokens_per_s": {"decode": round(nd / (ms * 1e-3), 1),
+                         "prefill": round(4 * 2048 / (ms * 1e-3), 1)},
+        "decode_bytes_per_step": int(dec_bytes),
     }
     print(json.dumps(line), flush=True)
 

@@ -56,31 +56,23 @@ struct TileRegs {
   uint4 v[4];  // 4 key rows x 8 d of one (key quad, d octet) unit
 };
 
+// Tile loads are buffer loads through per-prompt descriptors (SGPRs) whose
+// range ends at the prompt's last key row of this KV head, so rows past the
+// prompt read as zeros (no per-load branch).  Per-lane byte offsets are fixed
+// for the whole loop; the tile's first row goes in the scalar offset.
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillParams& p, int64_t krow0,
-                                          int n0, int L, int g) {
-  const int t = threadIdx.x;
-  const int64_t row = (int64_t)p.num_kv_heads * D;
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, __amdgpu_buffer_rsrc_t kr,
+                                          __amdgpu_buffer_rsrc_t vr, const uint32_t* koff,
+                                          const uint32_t* voff, uint32_t tile_off) {
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::KCH; ++i) {
-    const int idx = t + kThreads * i;
-    const int key = idx / (D / 8), ch = idx % (D / 8);
-    if (n0 + key < L)
-      r.k[i] = *reinterpret_cast<const uint4*>(p.k + (krow0 + n0 + key) * row + (int64_t)g * D + 8 * ch);
-    else
-      r.k[i] = make_uint4(0, 0, 0, 0);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], tile_off, 0);
+    r.k[i] = make_uint4(x.x, x.y, x.z, x.w);
   }
-  constexpr int units = (kN / 4) * (D / 8);
-  if (t < units) {
-    const int kq = t % (kN / 4), oc = t / (kN / 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 4 * kq + i;
-      if (n0 + key < L)
-        r.v[i] = *reinterpret_cast<const uint4*>(p.v + (krow0 + n0 + key) * row + (int64_t)g * D + 8 * oc);
-      else
-        r.v[i] = make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], tile_off, 0);
+    r.v[i] = make_uint4(x.x, x.y, x.z, x.w);
   }
 }
 
@@ -116,7 +108,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, int n_mtiles) {
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  __shared__ Smem<D> s;
+  __shared__ Smem<D> sbuf[2];  // double buffer: tile i computes from one while i+1 is stored
 
   // XCD-aware work mapping (see header).
   const int total = (int)(gridDim.x);
@@ -178,17 +170,38 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
 
   const int n_end = p.causal ? min(L, m0 + kM) : L;
   const int n_tiles = (n_end + kN - 1) / kN;
+  // buffer descriptors over this prompt's K/V rows of KV head g
+  const uint32_t rowb = (uint32_t)p.num_kv_heads * D * 2u;  // bytes per key row
+  const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2u;
+  const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
+  const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, span, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, span, kBufferFlags);
+  uint32_t koff[TileRegs<D>::KCH], voff[4];
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+    const int idx = threadIdx.x + kThreads * i;
+    koff[i] = (uint32_t)(idx / (D / 8)) * rowb + 16u * (idx % (D / 8));
+  }
+  {
+    constexpr int units = (kN / 4) * (D / 8);
+    const int t = threadIdx.x < units ? threadIdx.x : 0;
+    const int kq = t % (kN / 4), oc = t / (kN / 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)(4 * kq + i) * rowb + 16u * oc;
+  }
   TileRegs<D> tr;
-  load_tile<D>(tr, p, kv0, 0, L, g);
+  load_tile<D>(tr, kr, vr, koff, voff, 0u);
+  store_tile<D>(sbuf[0], tr);
+  __syncthreads();
 
   for (int it = 0; it < n_tiles; ++it) {
     const int n0 = it * kN;
-    __syncthreads();
-    store_tile<D>(s, tr);
-    __syncthreads();
-    if (it + 1 < n_tiles) load_tile<D>(tr, p, kv0, n0 + kN, L, g);
+    Smem<D>& s = sbuf[it & 1];
+    // the next tile's loads are in flight while this tile computes
+    if (it + 1 < n_tiles) load_tile<D>(tr, kr, vr, koff, voff, (uint32_t)(n0 + kN) * rowb);
 
-    if (p.causal && n0 > r0 + 31) continue;  // every key of the tile is after every row
+    if (!(p.causal && n0 > r0 + 31)) {  // skip tiles whose keys all follow this wavefront's rows
 
     // S^T = K . Q^T for two 32-key blocks
     f32x16 sacc[2];
@@ -203,14 +216,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
       }
     }
 
-    // scale to log2 units and mask (causal diagonal, prompt end)
+    // mask (causal diagonal, prompt end) on the raw scores; the log2-unit scale
+    // is folded into the exponent's fma below (scale > 0 keeps the max)
     const bool need_mask = (p.causal && n0 + kN - 1 > r0) || (n0 + kN > L);
-    float mx = kNegBig;
+    float mx = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = sacc[kb][r] * p.scale_log2;
+        float x = sacc[kb][r];
         if (need_mask) {
           const int key = n0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
           const bool vis = key < L && (!p.causal || key <= qpos);
@@ -220,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
         mx = fmaxf(mx, x);
       }
     }
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+    mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
     const float mnew = (mx > m + kTau) ? mx : m;
     if (__ballot(mnew != m)) {
       const float a = fast_exp2(m - mnew);
@@ -236,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(sacc[kb][r] - m);
+        const float pv = fast_exp2(__builtin_fmaf(sacc[kb][r], p.scale_log2, -m));
         l += pv;
         pb[kb * 2 + r / 8][r % 8] = (f16)pv;
       }
@@ -254,6 +268,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
         oacc[db] = mfma32(__builtin_bit_cast(f16x8, a4), pb[kk], oacc[db]);
       }
     }
+    }
+    // store the next tile into the other buffer; one barrier publishes it and
+    // guarantees every wavefront has finished reading the buffer it overwrites next
+    if (it + 1 < n_tiles) store_tile<D>(sbuf[(it + 1) & 1], tr);
+    __syncthreads();
   }
 
   // normalize and store rows of this lane's column

@@ -13,15 +13,17 @@ E4M3 codes with value scales, the writer's V error being FP8 rounding only.
 Readings taken where the pages leave it open:
   * append: token i goes to TARGET page slot_page[i], slot slot_index[i]; its
     K and V rows (all KV heads) are copied bit for bit;
-  * compaction of a page with n valid tokens (1..16), per KV head h:
-      scale[h] = fp32(absmax of the fp16 V over the n valid tokens x D) / 448
+  * a compact page is written from n consecutive source token rows
+    (0 <= n <= 16; the source is either the TARGET pool seen as rows, for a
+    demotion, or freshly computed K/V rows, for a prompt); per KV head h:
+      scale[h] = fp32(absmax of the fp16 V over the n rows x D) / 448
                  (one fp32 division, round to nearest even); 1.0 if absmax is 0
-      code     = E4M3FN(fp32(v) / scale[h]) for every slot of the page
+      code     = E4M3FN(fp32(v) / scale[h]) for slots 0..n-1
                  (fp32 division, then round to nearest even on the E4M3 grid;
                  magnitudes at or above 448 saturate to 448; NaN -> 0x7F)
-      K        = bit copy of every slot.
-    Valid rows must hold finite values; rows past n are encoded too, but
-    their contents do not enter the scale.
+      K        = bit copy of slots 0..n-1.
+    Slots n..15 are not read from the source (it may end there) and are
+    written as zeros (K +0.0, code 0x00).  Source rows must be finite.
 """
 import math
 
@@ -86,26 +88,33 @@ def encode_e4m3fn_array(x: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def compact_page(k16: np.ndarray, v16: np.ndarray, n_valid: int):
-    """One TARGET page (fp16 [16, Hkv, D] K and V) -> (K copy, E4M3 codes, fp32 scales [Hkv])."""
-    v32 = np.asarray(v16).astype(np.float32)
-    hkv = v32.shape[1]
+def quantize_page(k_rows: np.ndarray, v_rows: np.ndarray):
+    """n source rows (fp16 [n, Hkv, D] K and V, n <= 16) -> one compact page:
+    (K fp16 [16, Hkv, D], E4M3 codes u8 [16, Hkv, D], fp32 scales [Hkv])."""
+    k_rows = np.asarray(k_rows, dtype=np.float16)
+    v32 = np.asarray(v_rows, dtype=np.float16).astype(np.float32)
+    n, hkv, d = v32.shape
+    assert n <= 16
+    k = np.zeros((16, hkv, d), np.float16)
+    k[:n] = k_rows
+    codes = np.zeros((16, hkv, d), np.uint8)
     scale = np.empty(hkv, dtype=np.float32)
-    codes = np.empty(v32.shape, dtype=np.uint8)
     for h in range(hkv):
-        absmax = np.float32(np.abs(v32[:n_valid, h, :]).max()) if n_valid > 0 else np.float32(0)
+        absmax = np.float32(np.abs(v32[:, h, :]).max()) if n > 0 else np.float32(0)
         s = np.float32(absmax / np.float32(E4M3_MAX)) if absmax > 0 else np.float32(1.0)
         scale[h] = s
         q = (v32[:, h, :] / s).astype(np.float32)          # fp32 division, RNE
-        codes[:, h, :] = encode_e4m3fn_array(q)
-    return np.asarray(k16).copy(), codes, scale
+        codes[:n, h, :] = encode_e4m3fn_array(q)
+    return k, codes, scale
 
 
-def compact_pages(k_target, v_target, src_pages, n_valid):
-    """Compaction of the listed TARGET pages: returns (K, codes, scales) per page, stacked."""
+def quantize_pages(k_src, v_src, row_start, n_valid):
+    """Page i is written from rows row_start[i] .. row_start[i] + n_valid[i] - 1 of the
+    fp16 [rows, Hkv, D] source arrays; returns the stacked (K, codes, scales)."""
     ks, cs, ss = [], [], []
-    for p, n in zip(src_pages, n_valid):
-        k, c, s = compact_page(k_target[int(p)], v_target[int(p)], int(n))
+    for r, n in zip(row_start, n_valid):
+        r, n = int(r), int(n)
+        k, c, s = quantize_page(k_src[r:r + n], v_src[r:r + n])
         ks.append(k)
         cs.append(c)
         ss.append(s)

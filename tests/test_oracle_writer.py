@@ -12,8 +12,8 @@ import pytest
 import torch
 
 from oracle import E4M3FN_TABLE
-from oracle.writer import (append_tokens, compact_page, compact_pages, encode_e4m3fn,
-                           encode_e4m3fn_array)
+from oracle.writer import (append_tokens, encode_e4m3fn, encode_e4m3fn_array, quantize_page,
+                           quantize_pages)
 from mixed_precision_paged_amd import synth
 
 FINITE = [c for c in range(256) if not math.isnan(E4M3FN_TABLE[c])]
@@ -90,7 +90,7 @@ def test_scalar_and_array_forms_agree():
                                   np.array([encode_e4m3fn(float(v)) for v in x], np.uint8))
 
 
-# ---- page compaction -------------------------------------------------------------------------
+# ---- page quantization -------------------------------------------------------------------------
 
 def _page(rng, hkv=2, d=32, scale=1.0):
     k = rng.standard_normal((16, hkv, d)).astype(np.float16)
@@ -108,7 +108,7 @@ def test_exact_page_reconstructs_exactly():
     v = (E4M3FN_TABLE[codes] * s[None, :, None]).astype(np.float16)
     assert np.array_equal(v.astype(np.float64), E4M3FN_TABLE[codes] * s[None, :, None])  # exact in fp16
     k = rng.standard_normal((16, 2, 32)).astype(np.float16)
-    kk, c, sc = compact_page(k, v, 16)
+    kk, c, sc = quantize_page(k, v)
     np.testing.assert_array_equal(sc, s)
     want = codes.copy()
     np.testing.assert_array_equal(c, want)
@@ -120,7 +120,7 @@ def test_scale_is_absmax_over_448_and_peak_saturates_to_448():
     for trial in range(20):
         k, v = _page(rng, scale=rng.choice([1e-3, 1.0, 40.0]))
         n = int(rng.integers(1, 17))
-        _, c, s = compact_page(k, v, n)
+        _, c, s = quantize_page(k[:n], v[:n])
         for h in range(v.shape[1]):
             absmax = np.float32(np.abs(v[:n, h].astype(np.float32)).max())
             assert s[h] == np.float32(absmax / np.float32(448.0))
@@ -130,7 +130,7 @@ def test_scale_is_absmax_over_448_and_peak_saturates_to_448():
 def test_dequantized_error_within_half_an_e4m3_step():
     rng = np.random.default_rng(3)
     k, v = _page(rng, hkv=4, d=64, scale=3.0)
-    _, c, s = compact_page(k, v, 16)
+    _, c, s = quantize_page(k, v)
     x = v.astype(np.float64) / s[None, :, None]
     back = E4M3FN_TABLE[c]
     normal = np.abs(x) >= 2.0 ** -6
@@ -138,17 +138,36 @@ def test_dequantized_error_within_half_an_e4m3_step():
     assert np.all(np.abs(back - x)[~normal] <= 2.0 ** -10 * (1 + 1e-6))
 
 
-def test_rows_past_n_valid_do_not_enter_the_scale():
+def test_partial_page_reads_n_rows_and_zeroes_the_rest():
     rng = np.random.default_rng(4)
     k, v = _page(rng)
-    _, c1, s1 = compact_page(k, v, 9)
-    v2 = v.copy()
-    v2[9:] = np.float16(60000.0)
-    v2[12, 0, 0] = np.float16(np.nan)
-    _, c2, s2 = compact_page(k, v2, 9)
-    np.testing.assert_array_equal(s1, s2)
-    np.testing.assert_array_equal(c1[:9], c2[:9])
-    assert np.all((c2[9:] & 0x7F) >= 0x7E)   # saturated, or NaN
+    kk, c, s = quantize_page(k[:9], v[:9])
+    assert np.all(kk[9:].view(np.uint16) == 0) and np.all(c[9:] == 0)
+    np.testing.assert_array_equal(kk[:9].view(np.uint16), k[:9].view(np.uint16))
+    _, c16, _ = quantize_page(k, v)
+    full_max = np.abs(v.astype(np.float32)).max(axis=(0, 2))
+    part_max = np.abs(v[:9].astype(np.float32)).max(axis=(0, 2))
+    np.testing.assert_array_equal(s, (part_max / np.float32(448)).astype(np.float32))
+    if np.any(full_max != part_max):   # rows 9..15 raise some head's absmax
+        assert not np.array_equal(c16[:9], c[:9])
+
+
+def test_empty_page_is_zero_with_unit_scale():
+    kk, c, s = quantize_page(np.zeros((0, 3, 8), np.float16), np.zeros((0, 3, 8), np.float16))
+    assert np.all(kk.view(np.uint16) == 0) and np.all(c == 0) and np.all(s == 1.0)
+
+
+def test_pages_follow_row_starts():
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((40, 2, 16)).astype(np.float16)
+    v = rng.standard_normal((40, 2, 16)).astype(np.float16)
+    starts, ns = [0, 16, 32, 5], [16, 16, 8, 3]
+    K, C, S = quantize_pages(k, v, starts, ns)
+    for i, (r, n) in enumerate(zip(starts, ns)):
+        kk, c, s = quantize_page(k[r:r + n], v[r:r + n])
+        np.testing.assert_array_equal(K[i].view(np.uint16), kk.view(np.uint16))
+        np.testing.assert_array_equal(C[i], c)
+        np.testing.assert_array_equal(S[i], s)
 
 
 def test_zero_head_gets_unit_scale():
@@ -156,7 +175,7 @@ def test_zero_head_gets_unit_scale():
     k, v = _page(rng)
     v[:, 1] = np.float16(0.0)
     v[2, 1, 3] = np.float16(-0.0)
-    _, c, s = compact_page(k, v, 16)
+    _, c, s = quantize_page(k, v)
     assert s[1] == np.float32(1.0)
     assert np.all((c[:, 1] & 0x7F) == 0) and c[2, 1, 3] == 0x80
 
@@ -167,7 +186,7 @@ def test_agrees_with_library_quantizer_of_the_input_generator():
     v = (rng.standard_normal((5, 16, 2, 32)) * 7).astype(np.float16)
     k = rng.standard_normal((5, 16, 2, 32)).astype(np.float16)
     v[2] *= np.float16(1e-4)
-    _, c, s = compact_pages(k, v, np.arange(5), [16] * 5)
+    _, c, s = quantize_pages(k.reshape(80, 2, 32), v.reshape(80, 2, 32), np.arange(5) * 16, [16] * 5)
     lib_c, lib_s = synth.quantize_pages_e4m3(v, np.full(5, 16))
     np.testing.assert_array_equal(s, lib_s)
     np.testing.assert_array_equal(c, lib_c)

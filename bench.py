@@ -41,9 +41,11 @@ def parse():
     ap.add_argument("--no-flags", action="store_true", help="single-pool path (no per-page flag reads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time")
-    ap.add_argument("--workload", choices=("decode", "prefill", "mixed"), default="decode",
+    ap.add_argument("--workload", choices=("decode", "prefill", "mixed", "writer"), default="decode",
                     help="decode: the headline line; prefill: 32 x 8192 compact-prefill route "
-                         "(gather + causal prefill, 4 chunks); mixed: the 36-layer mixed batch")
+                         "(gather + causal prefill, 4 chunks); mixed: the 36-layer mixed batch; "
+                         "writer: cache writer (page quantizer over the 32 x 8192 prompt rows, "
+                         "TARGET append)")
     ap.add_argument("--layers", type=int, default=36, help="mixed workload: layers per step")
     ap.add_argument("--distinct-layers", type=int, default=4,
                     help="mixed workload: distinct generated layers cycled over the step")
@@ -74,6 +76,9 @@ def main():
         return
     if args.workload == "mixed":
         bench_mixed(args)
+        return
+    if args.workload == "writer":
+        bench_writer(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the decode hot path on a single MI355X "
@@ -324,6 +329,98 @@ def bench_mixed(args):
         "tokens_per_s": {"decode": round(nd / (ms * 1e-3), 1),
                          "prefill": round(4 * 2048 / (ms * 1e-3), 1)},
         "decode_bytes_per_step": int(dec_bytes),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_writer(args):
+    """Cache writer: quantize the 32 x 8192 prompt rows (FP16 K/V) into 16,384 compact pages
+    (K16 + E4M3 V + page-head scales), and append rows into TARGET pages (a 32-token decode
+    step, and one 65,536-token chunk of prompt rows)."""
+    import torch
+
+    from mixed_precision_paged_amd import bytemodel, ekv, synth
+
+    t0 = time.time()
+    c = synth.writer_prefill_case(seed=4)
+    gen_s = time.time() - t0
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    H, D = c.num_kv_heads, c.head_dim
+    kr, vr = dev(c.k_rows), dev(c.v_rows)
+    kc = torch.empty((c.n_compact_pages, 16, H, D), dtype=torch.float16, device="cuda")
+    vc = torch.empty((c.n_compact_pages, 16, H, D), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((c.n_compact_pages, H), dtype=torch.float32, device="cuda")
+    rs, dst, nv = dev(c.row_start), dev(c.dst_pages), dev(c.n_valid)
+    n_pages = int(c.row_start.size)
+    # TARGET pool for the appends: 4,096 pages, slots a seeded permutation
+    n_t = 4096
+    kt = torch.empty((n_t, 16, H, D), dtype=torch.float16, device="cuda")
+    vt = torch.empty_like(kt)
+    kv = ekv.paged_kv(H, D, kt, vt, kc, vc, sc)
+    slots = np.random.default_rng(40).permutation(n_t * 16).astype(np.int32)
+    chunk_tok = 65536
+    slot_chunk, slot_step = dev(slots[:chunk_tok]), dev(slots[:32])
+    assert slot_step.numel() == 32
+    k_step, v_step = kr[:32].contiguous(), vr[:32].contiguous()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        evs = _events(steps)
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+    steps = max(1, min(args.steps, 20))
+    tq = timed(lambda: ekv.ekv_quantize_pages(kv, kr, vr, rs, dst, nv, stream=stream), steps)
+    ta = timed(lambda: ekv.ekv_append_tokens(kv, kr[:chunk_tok], vr[:chunk_tok], slot_chunk,
+                                             stream=stream), steps)
+    td = timed(lambda: ekv.ekv_append_tokens(kv, k_step, v_step, slot_step, stream=stream), steps)
+    qr, qw = bytemodel.quantize_bytes(c.n_valid, H, D)
+    ar, aw = bytemodel.append_bytes(chunk_tok, H, D)
+    gbps = (qr + qw) / tq / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle  # CPU baseline leg only
+
+        reps, sample = 0, 64
+        t1 = time.perf_counter()
+        while True:
+            oracle.quantize_pages(c.k_rows, c.v_rows, c.row_start[:sample], c.n_valid[:sample])
+            reps += 1
+            el = time.perf_counter() - t1
+            if el >= args.cpu_seconds / 2:
+                break
+        sr, sw = bytemodel.quantize_bytes(c.n_valid[:sample], H, D)
+        cpu = {"value": round((sr + sw) * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"the first {sample} of the 16,384 pages quantized {reps}x by the oracle "
+                         f"in {el:.1f} s (numpy, one thread)"}
+    line = {
+        "metric": "cache writer: page-quantizer HBM GB/s (FP16 rows -> K16 + E4M3 V pages)",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(tq * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16->e4m3", "data": "synthetic",
+        "config": {"workload": "cache writer: 32 prompts x 8192 tokens of FP16 K/V rows (8 KV heads, "
+                               "head dim 128, seed 4) quantized into 16,384 compact pages of a "
+                               "17,408-page pool; TARGET append of 65,536 rows and of a 32-token "
+                               "decode step into a 4,096-page pool",
+                   "pages": n_pages, "num_kv_heads": H, "head_dim": D},
+        "roofline": {"bound": "hbm", "kernel": "ekv_quantize_pages (quantize_kernel<128>)",
+                     "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_call_us": round(tq * 1e6, 2), "algorithmic_bytes": qr + qw},
+        "append": {"tokens": chunk_tok, "avg_call_us": round(ta * 1e6, 2),
+                   "gbps": round((ar + aw) / ta / 1e9, 1),
+                   "frac": round((ar + aw) / ta / 1e9 / HBM_PEAK_GBPS, 4),
+                   "decode_step_32_tokens_us": round(td * 1e6, 2)},
+        "cpu_baseline": cpu,
+        "input_generation_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
 

@@ -215,6 +215,56 @@ ekv_status ekv_prefill_attention(const void* q, int32_t q_rows, const void* k, c
                                  float* lse, void* stream);
 
 /*
+ * Cache writer, TARGET append: store new tokens' K and V rows into TARGET
+ * pages.  [ekv] section 3.2 and appendix B.3: newly appended KV is kept at
+ * target fidelity in the protected recent window.
+ *
+ *   kv           the layer's pools; this call WRITES through kv->k_target and
+ *                kv->v_target (writable device memory; n_target_pages * 16
+ *                must be below 2^31).
+ *   k_new, v_new fp16 [n_tokens][num_kv_heads][head_dim] (device).
+ *   slot_mapping int32 [n_tokens] (device): token t goes to TARGET page
+ *                slot_mapping[t] / 16, slot slot_mapping[t] % 16; all KV heads
+ *                of the row are copied bit for bit.  A negative or
+ *                out-of-pool slot skips that token.  Slots must be distinct
+ *                (two tokens on one slot race).
+ */
+ekv_status ekv_append_tokens(const ekv_paged_kv* kv, const void* k_new, const void* v_new,
+                             const int32_t* slot_mapping, int32_t n_tokens, void* stream);
+
+/*
+ * Cache writer, page quantizer: write compact pages (K16 + E4M3 V + scale)
+ * from FP16 token rows, with the scale finalized over the whole page.
+ * [asym] "What changes in vLLM's prefill routing?" and the table "Historical
+ * reported implementation checks": keys stay bit-exact, values become E4M3
+ * with value scales.  [ekv] section 3.3: a TARGET -> compact transition
+ * rewrites whole pages.  One call serves a demotion (source = the TARGET
+ * pool seen as rows, row = page * 16) and a prompt's fresh rows.
+ *
+ *   kv             the layer's pools; this call WRITES through kv->k_compact,
+ *                  kv->v_compact and kv->v_scale (writable device memory).
+ *   k_src, v_src   fp16 [src_rows][num_kv_heads][head_dim] (device); must not
+ *                  overlap the compact pool.
+ *   src_row_start  int32 [n_pages]: page i is made of source rows
+ *                  src_row_start[i] .. src_row_start[i] + n_valid[i] - 1.
+ *   n_valid        int32 [n_pages] in 0..16, or NULL for 16 each.
+ *   dst_pages      int32 [n_pages]: compact page ids written (distinct).
+ * Per KV head h of page i, with absmax over the n_valid rows x head_dim:
+ *   v_scale[dst][h] = absmax / 448 (fp32, round to nearest even), or 1.0
+ *                     when absmax is 0;
+ *   code = E4M3FN(fp32(v) / scale): correctly rounded fp32 quotient, then the
+ *          nearest E4M3 value, ties to even, saturating at +-448, NaN -> 0x7F;
+ *   K    = bit copy.  Slots past n_valid get K = +0.0 and code 0x00.
+ * Source rows must hold finite values.  A page whose rows leave [0,
+ * src_rows), whose n_valid is outside 0..16 or whose dst id is outside the
+ * compact pool is skipped (nothing is written for it).
+ */
+ekv_status ekv_quantize_pages(const ekv_paged_kv* kv, const void* k_src, const void* v_src,
+                              int64_t src_rows, const int32_t* src_row_start,
+                              const int32_t* n_valid, const int32_t* dst_pages, int32_t n_pages,
+                              void* stream);
+
+/*
  * Diagnostic for the device E4M3 decoding used by the kernels: converts n
  * codes to fp16.  method 0 = the decode kernel's path (codes packed four per
  * 32-bit word, scale 1), 2 = the same path with scale 2^-7 (so out =

@@ -74,6 +74,25 @@ def gather_bytes(n_pages: int, num_kv_heads: int, head_dim: int):
     return read, written
 
 
+def quantize_bytes(n_valid, num_kv_heads: int, head_dim: int, n_valid_read: bool = True):
+    """(read, written) bytes of one page-quantizer launch over pages holding ``n_valid``
+    rows each: the valid rows' K16 + V16 (4 B per pair) and the per-page int32 entries
+    (row start, destination id, row count) are read; whole pages of K16 + E4M3 V (3 B per
+    pair, all 16 slots) and one fp32 scale per page and KV head are written."""
+    n_valid = np.asarray(n_valid, dtype=np.int64)
+    hd = num_kv_heads * head_dim
+    n_pages = int(n_valid.size)
+    read = int(n_valid.sum()) * hd * 4 + n_pages * (12 if n_valid_read else 8)
+    written = n_pages * PAGE * hd * 3 + n_pages * num_kv_heads * 4
+    return read, written
+
+
+def append_bytes(n_tokens: int, num_kv_heads: int, head_dim: int):
+    """(read, written) bytes of one TARGET append: K16 + V16 rows and one int32 slot each."""
+    hd = num_kv_heads * head_dim
+    return n_tokens * (hd * 4 + 4), n_tokens * hd * 4
+
+
 def prefill_flops(prompt_lens, num_q_heads: int, head_dim: int, causal: bool = True) -> int:
     """Dense QK^T + PV FLOPs (masked-out pairs not counted)."""
     total = 0

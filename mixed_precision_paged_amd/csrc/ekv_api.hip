@@ -262,6 +262,65 @@ ekv_status ekv_prefill_attention(const void* q, int32_t q_rows, const void* k, c
   return hip_status(ekv::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
+ekv_status ekv_append_tokens(const ekv_paged_kv* kv, const void* k_new, const void* v_new,
+                             const int32_t* slot_mapping, int32_t n_tokens, void* stream) {
+  if (!kv) return fail(EKV_ERR_INVALID_ARG, "kv descriptor is NULL");
+  if (kv->head_dim != 64 && kv->head_dim != 128) return fail(EKV_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", kv->head_dim);
+  if (kv->num_kv_heads <= 0) return fail(EKV_ERR_INVALID_ARG, "num_kv_heads must be positive");
+  ekv_status s = check_kv(kv, true, false);
+  if (s != EKV_OK) return s;
+  if ((int64_t)kv->n_target_pages * EKV_PAGE_SIZE > 0x7FFFFFFFLL)
+    return fail(EKV_ERR_UNSUPPORTED, "target pool of %d pages exceeds int32 slot numbers", kv->n_target_pages);
+  if (n_tokens < 0) return fail(EKV_ERR_INVALID_ARG, "n_tokens %d < 0", n_tokens);
+  if (n_tokens == 0) return ok();
+  if (!k_new || !v_new || !slot_mapping) return fail(EKV_ERR_INVALID_ARG, "k_new, v_new and slot_mapping are required");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(EKV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  ekv::AppendParams p{};
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.slot_mapping = slot_mapping;
+  p.n_tokens = n_tokens;
+  p.k_target = static_cast<uint16_t*>(const_cast<void*>(kv->k_target));
+  p.v_target = static_cast<uint16_t*>(const_cast<void*>(kv->v_target));
+  p.n_target = kv->n_target_pages;
+  p.num_kv_heads = kv->num_kv_heads;
+  p.head_dim = kv->head_dim;
+  return hip_status(ekv::launch_append(p, static_cast<hipStream_t>(stream)), "append launch");
+}
+
+ekv_status ekv_quantize_pages(const ekv_paged_kv* kv, const void* k_src, const void* v_src,
+                              int64_t src_rows, const int32_t* src_row_start,
+                              const int32_t* n_valid, const int32_t* dst_pages, int32_t n_pages,
+                              void* stream) {
+  if (!kv) return fail(EKV_ERR_INVALID_ARG, "kv descriptor is NULL");
+  if (kv->head_dim != 64 && kv->head_dim != 128) return fail(EKV_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", kv->head_dim);
+  if (kv->num_kv_heads <= 0) return fail(EKV_ERR_INVALID_ARG, "num_kv_heads must be positive");
+  if ((int64_t)kv->num_kv_heads * kv->head_dim * 2 * EKV_PAGE_SIZE > 0x7FFFFFFFLL)
+    return fail(EKV_ERR_UNSUPPORTED, "page of %d KV heads too large", kv->num_kv_heads);
+  ekv_status s = check_kv(kv, false, true);
+  if (s != EKV_OK) return s;
+  if (n_pages < 0 || src_rows < 0) return fail(EKV_ERR_INVALID_ARG, "negative size");
+  if (n_pages == 0) return ok();
+  if (!k_src || !v_src || !src_row_start || !dst_pages)
+    return fail(EKV_ERR_INVALID_ARG, "k_src, v_src, src_row_start and dst_pages are required");
+  if (!aligned16(k_src) || !aligned16(v_src)) return fail(EKV_ERR_INVALID_ARG, "k_src and v_src must be 16-byte aligned");
+  ekv::QuantizeParams p{};
+  p.k_src = static_cast<const uint16_t*>(k_src);
+  p.v_src = static_cast<const uint16_t*>(v_src);
+  p.src_rows = src_rows;
+  p.src_row_start = src_row_start;
+  p.n_valid = n_valid;
+  p.dst_pages = dst_pages;
+  p.n_pages = n_pages;
+  p.k_compact = static_cast<uint16_t*>(const_cast<void*>(kv->k_compact));
+  p.v_compact = const_cast<uint8_t*>(kv->v_compact);
+  p.v_scale = const_cast<float*>(kv->v_scale);
+  p.n_compact = kv->n_compact_pages;
+  p.num_kv_heads = kv->num_kv_heads;
+  p.head_dim = kv->head_dim;
+  return hip_status(ekv::launch_quantize(p, static_cast<hipStream_t>(stream)), "quantize launch");
+}
+
 ekv_status ekv_e4m3_to_f16(const uint8_t* codes, int32_t n, void* out, int32_t method, void* stream) {
   if (n < 0) return fail(EKV_ERR_INVALID_ARG, "n %d < 0", n);
   if (method < 0 || method > 2) return fail(EKV_ERR_INVALID_ARG, "method must be 0, 1 or 2");

@@ -61,6 +61,32 @@ struct PrefillParams {
   float* lse;
 };
 
+struct AppendParams {
+  const uint16_t* k_new;        // [n_tokens][Hkv][D]
+  const uint16_t* v_new;
+  const int32_t* slot_mapping;  // [n_tokens], page * 16 + slot
+  int64_t n_tokens;
+  uint16_t* k_target;
+  uint16_t* v_target;
+  int32_t n_target;
+  int32_t num_kv_heads, head_dim;
+};
+
+struct QuantizeParams {
+  const uint16_t* k_src;        // [src_rows][Hkv][D]
+  const uint16_t* v_src;
+  int64_t src_rows;
+  const int32_t* src_row_start;  // [n_pages]
+  const int32_t* n_valid;        // [n_pages] or NULL (16 each)
+  const int32_t* dst_pages;      // [n_pages]
+  int32_t n_pages;
+  uint16_t* k_compact;
+  uint8_t* v_compact;
+  float* v_scale;
+  int32_t n_compact;
+  int32_t num_kv_heads, head_dim;
+};
+
 // Split plan shared by the scratch query and the launch.
 int32_t decode_auto_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages);
 size_t decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -69,6 +95,8 @@ size_t decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_h
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
 hipError_t launch_e4m3_to_f16(const uint8_t* codes, int32_t n, uint16_t* out, int32_t method,
                               hipStream_t stream);
 

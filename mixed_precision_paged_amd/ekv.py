@@ -37,7 +37,7 @@ EXPORTED = (
     "ekv_abi_version", "ekv_status_string", "ekv_last_error", "ekv_decode_pages_per_split",
     "ekv_decode_plan_pages_per_split",
     "ekv_decode_scratch_bytes", "ekv_decode_attention", "ekv_gather_compact_pages",
-    "ekv_prefill_attention", "ekv_e4m3_to_f16",
+    "ekv_prefill_attention", "ekv_append_tokens", "ekv_quantize_pages", "ekv_e4m3_to_f16",
 )
 
 
@@ -71,6 +71,11 @@ _lib.ekv_prefill_attention.restype = ctypes.c_int
 _lib.ekv_prefill_attention.argtypes = [
     _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, ctypes.c_int,
     _vp, _vp]
+_lib.ekv_append_tokens.restype = ctypes.c_int
+_lib.ekv_append_tokens.argtypes = [ctypes.POINTER(PagedKV), _vp, _vp, _vp, _i32, _vp]
+_lib.ekv_quantize_pages.restype = ctypes.c_int
+_lib.ekv_quantize_pages.argtypes = [ctypes.POINTER(PagedKV), _vp, _vp, ctypes.c_int64, _vp, _vp, _vp,
+                                    _i32, _vp]
 _lib.ekv_e4m3_to_f16.restype = ctypes.c_int
 _lib.ekv_e4m3_to_f16.argtypes = [_vp, _i32, _vp, _i32, _vp]
 
@@ -194,6 +199,38 @@ def ekv_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _ptr(q), q_rows, _ptr(k), _ptr(v), kv_rows, _ptr(cu_seqlens_q), _ptr(kv_start),
         int(kv_start.shape[0]), int(max_len), hq, hkv, d, 1 if causal else 0, float(sm_scale),
         _ptr(out), _dtype_code(out), _ptr(lse), _stream(stream)))
+
+
+def ekv_append_tokens(kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor,
+                      slot_mapping: torch.Tensor, stream=None) -> None:
+    """Write new tokens' K/V rows ([n, Hkv, D] fp16) into TARGET slots (see ekv.h).
+    ``kv`` must describe writable TARGET pools."""
+    for t in (k_new, v_new):
+        if t.dtype != torch.float16:
+            raise TypeError(f"new K/V rows have dtype {t.dtype}, expected float16")
+    if slot_mapping.dtype != torch.int32:
+        raise TypeError("slot_mapping must be int32")
+    _check(_lib.ekv_append_tokens(ctypes.byref(kv), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                                  int(slot_mapping.shape[0]), _stream(stream)))
+
+
+def ekv_quantize_pages(kv: PagedKV, k_src: torch.Tensor, v_src: torch.Tensor,
+                       src_row_start: torch.Tensor, dst_pages: torch.Tensor,
+                       n_valid: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Write compact pages (K16 + E4M3 V + per-page-per-head scale) from fp16 rows (see ekv.h).
+
+    k_src, v_src: [rows, Hkv, D] (or the TARGET pool view [pages, 16, Hkv, D]).
+    ``kv`` must describe writable compact pools."""
+    for t in (k_src, v_src):
+        if t.dtype != torch.float16:
+            raise TypeError(f"source rows have dtype {t.dtype}, expected float16")
+    for t in (src_row_start, dst_pages, n_valid):
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError("src_row_start, dst_pages and n_valid must be int32")
+    rows = k_src.numel() // (kv.num_kv_heads * kv.head_dim)
+    _check(_lib.ekv_quantize_pages(ctypes.byref(kv), _ptr(k_src), _ptr(v_src), rows,
+                                   _ptr(src_row_start), _ptr(n_valid), _ptr(dst_pages),
+                                   int(dst_pages.shape[0]), _stream(stream)))
 
 
 def ekv_e4m3_to_f16(codes: torch.Tensor, out: torch.Tensor, method: int, stream=None) -> None:

@@ -340,3 +340,53 @@ def mixed_batch_layer(layer: int, n_decode: int = 32, lo: int = 4096, hi: int = 
                            prompt_lens=np.full(n_prompts, prompt_len, dtype=np.int32),
                            q_decode=paged.q[:n_decode], q_prefill=paged.q[n_decode:],
                            cu_seqlens_q=cu)
+
+
+@dataclasses.dataclass
+class WriterCase:
+    """Fresh FP16 K/V rows of packed prompts, cut into pages for the cache writer."""
+
+    k_rows: np.ndarray            # fp16 [T, Hkv, D]
+    v_rows: np.ndarray            # fp16 [T, Hkv, D]
+    prompt_lens: np.ndarray       # int32 [n]
+    row_start: np.ndarray         # int32 [n_pages]: first row of each page
+    n_valid: np.ndarray           # int32 [n_pages]: rows in each page (16, or fewer at a prompt's end)
+    dst_pages: np.ndarray         # int32 [n_pages]: distinct compact-pool ids (seeded permutation)
+    n_compact_pages: int          # pool size: pages + 6.25% slack
+    num_kv_heads: int
+    head_dim: int
+
+
+def make_writer_case(seed: int, prompt_lens: Sequence[int], num_kv_heads: int, head_dim: int,
+                     outlier_frac: float = 0.0, outlier_mult: float = 1.0,
+                     slack_frac: float = 0.0625) -> WriterCase:
+    """K then V rows drawn like pool pages (256 pages of rows at a time), trimmed to the
+    prompts' total length; then the pool permutation for the destination ids."""
+    rng = _rng(seed)
+    lens = np.asarray(prompt_lens, dtype=np.int64)
+    T = int(lens.sum())
+    row_pages = (T + PAGE_SIZE - 1) // PAGE_SIZE
+    k = _pool_fp16(rng, row_pages, num_kv_heads, head_dim, 0.0, 1.0)
+    k = k.reshape(-1, num_kv_heads, head_dim)[:T]
+    v = _pool_fp16(rng, row_pages, num_kv_heads, head_dim, outlier_frac, outlier_mult)
+    v = v.reshape(-1, num_kv_heads, head_dim)[:T]
+    starts, valid = [], []
+    row = 0
+    for n in lens:
+        j = np.arange((int(n) + PAGE_SIZE - 1) // PAGE_SIZE)
+        starts.append(row + PAGE_SIZE * j)
+        valid.append(np.minimum(PAGE_SIZE, int(n) - PAGE_SIZE * j))
+        row += int(n)
+    row_start = np.concatenate(starts).astype(np.int32) if starts else np.zeros(0, np.int32)
+    n_valid = np.concatenate(valid).astype(np.int32) if valid else np.zeros(0, np.int32)
+    n_pool = _pool_size(row_start.size, None, slack_frac)
+    dst = rng.permutation(n_pool)[:row_start.size].astype(np.int32)
+    return WriterCase(k_rows=k, v_rows=v, prompt_lens=lens.astype(np.int32), row_start=row_start,
+                      n_valid=n_valid, dst_pages=dst, n_compact_pages=n_pool,
+                      num_kv_heads=num_kv_heads, head_dim=head_dim)
+
+
+def writer_prefill_case(seed: int = 4, prompts: int = 32, length: int = 8192) -> WriterCase:
+    """The compact-prefill prompt set (32 x 8192 tokens, 8 KV heads, D 128) written
+    into 16,384 compact pages of a 17,408-page pool."""
+    return make_writer_case(seed, [length] * prompts, 8, 128)

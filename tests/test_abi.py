@@ -22,7 +22,7 @@ def _declared():
 
 def test_every_declared_function_is_exported():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(ekv._lib, n), n
     assert sorted(ekv.EXPORTED) == names
@@ -135,3 +135,28 @@ def test_e4m3_diagnostic_validation():
     assert f(FAKE, 4, FAKE, 3, None) == ekv.EKV_ERR_INVALID_ARG
     assert f(None, 4, FAKE, 0, None) == ekv.EKV_ERR_INVALID_ARG
     assert f(FAKE, 0, FAKE, 0, None) == ekv.EKV_OK
+
+
+def test_append_validation():
+    f = ekv._lib.ekv_append_tokens
+    kv_t = _kv(n_t=64, n_c=0)
+    assert f(ctypes.byref(_kv(n_t=0, n_c=5)), FAKE, FAKE, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(kv_t), None, FAKE, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(kv_t), FAKE + 8, FAKE, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(kv_t), FAKE, FAKE, FAKE, -1, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(_kv(d=96, n_t=64)), FAKE, FAKE, FAKE, 4, None) == ekv.EKV_ERR_UNSUPPORTED
+    assert f(ctypes.byref(_kv(n_t=1 << 28, n_c=0)), FAKE, FAKE, FAKE, 4, None) == ekv.EKV_ERR_UNSUPPORTED
+    assert f(None, FAKE, FAKE, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(kv_t), FAKE, FAKE, FAKE, 0, None) == ekv.EKV_OK
+
+
+def test_quantize_validation():
+    f = ekv._lib.ekv_quantize_pages
+    kv = _kv()
+    assert f(ctypes.byref(_kv(n_t=5, n_c=0)), FAKE, FAKE, 64, FAKE, None, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(kv), FAKE, FAKE, 64, None, None, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(kv), FAKE, FAKE, 64, FAKE, None, None, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(kv), FAKE, FAKE + 4, 64, FAKE, None, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(kv), FAKE, FAKE, -1, FAKE, None, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(_kv(d=32)), FAKE, FAKE, 64, FAKE, None, FAKE, 4, None) == ekv.EKV_ERR_UNSUPPORTED
+    assert f(ctypes.byref(kv), FAKE, FAKE, 64, FAKE, None, FAKE, 0, None) == ekv.EKV_OK

@@ -62,3 +62,18 @@ def test_decode_bytes_counts_target_values_twice_and_partial_pages():
 def test_prefill_flops():
     assert bytemodel.prefill_flops([8192] * 32, 32, 128) == 32 * 2 * 128 * 32 * 8192 * 8193
     assert bytemodel.prefill_flops([3], 1, 1, causal=False) == 4 * 9
+
+
+def test_writer_bytes_closed_forms():
+    """Quantizer: 4 B read and 3 B written per K/V pair; the 32 x 8192 prompt set is
+    16,384 full pages of 8 heads x 128 (268,435,456 pairs)."""
+    pairs = 16384 * 16 * 8 * 128
+    rd, wr = bytemodel.quantize_bytes(np.full(16384, 16), 8, 128)
+    assert rd == 4 * pairs + 16384 * 12 == 1_073_938_432
+    assert wr == 3 * pairs + 16384 * 8 * 4 == 805_830_656
+    rd0, _ = bytemodel.quantize_bytes(np.full(16384, 16), 8, 128, n_valid_read=False)
+    assert rd - rd0 == 16384 * 4
+    # a partial page reads only its rows, but writes all 16 slots
+    rd1, wr1 = bytemodel.quantize_bytes([5], 2, 64)
+    assert rd1 == 5 * 2 * 64 * 4 + 12 and wr1 == 16 * 2 * 64 * 3 + 2 * 4
+    assert bytemodel.append_bytes(32, 8, 128) == (32 * (4096 + 4), 32 * 4096)

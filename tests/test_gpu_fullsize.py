@@ -130,3 +130,32 @@ def test_mixed_batch_one_layer_routed():
                                        L.cu_seqlens_q, kv_start, True, c.sm_scale, rows=sample)
     assert_close(o[nd:][sample], pw[sample], what="prefill rows")
     assert_lse_close(ls[nd:][sample], plw[sample])
+
+
+def test_writer_quantizes_32x8192_prompts_into_16384_pages():
+    """The prefill writer at full size, in the bench's launch: sampled pages bit-exact against
+    the oracle; on every page, K equals the source rows and each head's peak code is +-448."""
+    step("fullsize writer: quantize 32 x 8192 prompt rows into 16,384 compact pages")
+    c = synth.writer_prefill_case(seed=4)
+    H, D = c.num_kv_heads, c.head_dim
+    kr, vr = dev(c.k_rows), dev(c.v_rows)
+    kc = torch.empty((c.n_compact_pages, 16, H, D), dtype=torch.float16, device="cuda")
+    vc = torch.empty((c.n_compact_pages, 16, H, D), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((c.n_compact_pages, H), dtype=torch.float32, device="cuda")
+    kv = ekv().paged_kv(H, D, k_compact=kc, v_compact=vc, v_scale=sc)
+    dst = dev(c.dst_pages)
+    ekv().ekv_quantize_pages(kv, kr, vr, dev(c.row_start), dst, dev(c.n_valid))
+    torch.cuda.synchronize()
+    idx = dst.long()
+    assert torch.equal(kc[idx].view(torch.int16).reshape(-1), kr.view(torch.int16).reshape(-1))
+    peak = (vc[idx] & 0x7F).amax(dim=(1, 3))
+    assert bool((peak == 0x7E).all())
+    rng = np.random.default_rng(46)
+    sample = np.concatenate([[0, 1, len(c.dst_pages) - 1], rng.choice(len(c.dst_pages), 61, replace=False)])
+    got_k = kc[idx[dev(sample).long()]].cpu().numpy()
+    got_v = vc[idx[dev(sample).long()]].cpu().numpy()
+    got_s = sc[idx[dev(sample).long()]].cpu().numpy()
+    K, V, S = oracle.quantize_pages(c.k_rows, c.v_rows, c.row_start[sample], c.n_valid[sample])
+    assert np.array_equal(got_k.view(np.uint16), K.view(np.uint16))
+    assert np.array_equal(got_v, V)
+    assert np.array_equal(got_s.view(np.uint32), S.view(np.uint32))

@@ -27,11 +27,12 @@ from .e4m3 import E4M3FN_TABLE, e4m3fn_value, decode_e4m3fn
 from .paged import sequence_kv
 from .attention import attention_rows, decode_attention, prefill_attention
 from .gather import gather_compact_pages
+from .paged_prefill import paged_prefill_attention, prompt_rows
 from .writer import append_tokens, encode_e4m3fn, encode_e4m3fn_array, quantize_page, quantize_pages
 
 __all__ = [
     "E4M3FN_TABLE", "e4m3fn_value", "decode_e4m3fn", "sequence_kv",
     "attention_rows", "decode_attention", "prefill_attention",
     "gather_compact_pages", "append_tokens", "quantize_page", "quantize_pages",
-    "encode_e4m3fn", "encode_e4m3fn_array",
+    "encode_e4m3fn", "encode_e4m3fn_array", "paged_prefill_attention", "prompt_rows",
 ]

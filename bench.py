@@ -240,6 +240,24 @@ def bench_prefill(args):
         g_ms += [a.elapsed_time(b) for a, b in evg]
         p_ms += [a.elapsed_time(b) for a, b in evp]
     wall = (time.perf_counter() - t0) / steps
+    # direct route: all 32 prompts from their pages in one launch, no workspace
+    pt, cu_all = dev(c.page_table), dev(pc.cu_seqlens_q)
+
+    def run_paged():
+        ekv.ekv_prefill_paged_attention(kv, q, cu_all, pt, None, 8192, c.sm_scale, out, stream=stream)
+
+    for _ in range(max(1, args.warmup // 2)):
+        run_paged()
+    torch.cuda.synchronize()
+    d_ms = []
+    for _ in range(steps):
+        (a, b), = _events(1)
+        a.record(stream)
+        run_paged()
+        b.record(stream)
+        torch.cuda.synchronize()
+        d_ms.append(a.elapsed_time(b))
+    d = float(np.mean(d_ms)) * 1e-3
     rd, wr = bytemodel.gather_bytes(4096, H, D)
     flops = bytemodel.prefill_flops([8192] * 8, Hq, D, causal=True)
     g = float(np.mean(g_ms)) * 1e-3
@@ -257,6 +275,12 @@ def bench_prefill(args):
         "gather": {"avg_chunk_us": round(g * 1e6, 1), "bytes_per_chunk": rd + wr,
                    "gbps": round((rd + wr) / g / 1e9, 1), "peak_gbps": HBM_PEAK_GBPS,
                    "frac": round((rd + wr) / g / 1e9 / HBM_PEAK_GBPS, 4)},
+        "direct_paged": {"kernel": "ekv_prefill_paged_attention (prefill_kernel<128, paged>)",
+                         "prompts_per_launch": 32, "avg_ms": round(d * 1e3, 3),
+                         "tflops": round(4 * flops / d / 1e12, 1),
+                         "mfma_frac": round(4 * flops / d / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+                         "gather_route_ms_same_work": round(4 * (g + p) * 1e3, 3),
+                         "speedup_vs_gather_route": round(4 * (g + p) / d, 4)},
     }
     print(json.dumps(line), flush=True)
 

@@ -215,6 +215,35 @@ ekv_status ekv_prefill_attention(const void* q, int32_t q_rows, const void* k, c
                                  float* lse, void* stream);
 
 /*
+ * Direct paged prefill: causal FP16 prefill of fresh prompts that reads each
+ * prompt's own pages (no workspace).  [asym] "Existing fallback: mixed-type
+ * prefill" (a prefill kernel on stored K16/V8 pages) and "What changes in
+ * vLLM's prefill routing?" (the gather route this replaces); [ekv] section
+ * 3.2 (TARGET and compact pages read in one launch).
+ *
+ *   q            fp16 [q_rows][num_q_heads][head_dim]; prompt p owns rows
+ *                [cu_seqlens_q[p], cu_seqlens_q[p+1]) (device int32 [n+1]).
+ *   page_table   int32 [n_prompts][pt_stride] (device): token t of prompt p
+ *                is in page page_table[p][t/16], slot t%16; q_len == kv_len.
+ *   fidelity     u8 [n_prompts][pt_stride] or NULL when exactly one pool is
+ *                given (as in ekv_decode_attention).
+ *   max_len      host bound of every prompt length; > EKV_MAX_PREFILL_TOKENS
+ *                returns EKV_ERR_NOT_ELIGIBLE; pt_stride >= ceil(max_len/16).
+ *   causal, sm_scale, out, out_dtype, lse: as in ekv_prefill_attention.
+ * Values: a TARGET page's FP16 V as stored; a compact page's V as
+ * fp16(fp32(e4m3) * fp32(scale)) — the scaled gather's values, so the result
+ * equals gather + ekv_prefill_attention bit for bit.  A 128-row tile of a
+ * prompt whose keys include an out-of-pool page id or an unknown flag is
+ * written as NaN; an over-long prompt (len > max_len) is written as NaN.
+ */
+ekv_status ekv_prefill_paged_attention(const ekv_paged_kv* kv, const void* q, int32_t q_rows,
+                                       const int32_t* cu_seqlens_q, const int32_t* page_table,
+                                       int32_t pt_stride, const uint8_t* fidelity, int32_t n_prompts,
+                                       int32_t max_len, int32_t num_q_heads, int32_t causal,
+                                       float sm_scale, void* out, ekv_dtype out_dtype, float* lse,
+                                       void* stream);
+
+/*
  * Cache writer, TARGET append: store new tokens' K and V rows into TARGET
  * pages.  [ekv] section 3.2 and appendix B.3: newly appended KV is kept at
  * target fidelity in the protected recent window.

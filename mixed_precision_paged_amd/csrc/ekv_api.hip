@@ -262,6 +262,65 @@ ekv_status ekv_prefill_attention(const void* q, int32_t q_rows, const void* k, c
   return hip_status(ekv::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
+ekv_status ekv_prefill_paged_attention(const ekv_paged_kv* kv, const void* q, int32_t q_rows,
+                                       const int32_t* cu_seqlens_q, const int32_t* page_table,
+                                       int32_t pt_stride, const uint8_t* fidelity, int32_t n_prompts,
+                                       int32_t max_len, int32_t num_q_heads, int32_t causal,
+                                       float sm_scale, void* out, ekv_dtype out_dtype, float* lse,
+                                       void* stream) {
+  if (!kv) return fail(EKV_ERR_INVALID_ARG, "kv descriptor is NULL");
+  ekv_status s = check_geometry(num_q_heads, kv->num_kv_heads, kv->head_dim);
+  if (s != EKV_OK) return s;
+  s = check_kv(kv, false, false);
+  if (s != EKV_OK) return s;
+  if (n_prompts < 0 || max_len < 0 || q_rows < 0) return fail(EKV_ERR_INVALID_ARG, "negative size");
+  if (max_len > EKV_MAX_PREFILL_TOKENS)
+    return fail(EKV_ERR_NOT_ELIGIBLE, "prompt bound %d exceeds %d tokens", max_len, EKV_MAX_PREFILL_TOKENS);
+  if (causal != 0 && causal != 1) return fail(EKV_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (out_dtype != EKV_F16 && out_dtype != EKV_F32) return fail(EKV_ERR_INVALID_ARG, "out_dtype %d unknown", (int)out_dtype);
+  if (!std::isfinite(sm_scale)) return fail(EKV_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (n_prompts == 0 || max_len == 0) return ok();
+  if (!q || !cu_seqlens_q || !page_table || !out)
+    return fail(EKV_ERR_INVALID_ARG, "q, cu_seqlens_q, page_table and out are required");
+  if (!aligned16(q) || !aligned16(out)) return fail(EKV_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (pt_stride < ceil_div(max_len, EKV_PAGE_SIZE))
+    return fail(EKV_ERR_INVALID_ARG, "pt_stride %d < ceil(max_len/16) = %d", pt_stride, ceil_div(max_len, EKV_PAGE_SIZE));
+  const bool has_t = kv->n_target_pages > 0, has_c = kv->n_compact_pages > 0;
+  int32_t uniform_kind = 0;
+  if (!fidelity) {
+    if (has_t == has_c) return fail(EKV_ERR_INVALID_ARG, "fidelity may be NULL only when exactly one pool is non-empty");
+    uniform_kind = has_c ? EKV_FIDELITY_COMPACT : EKV_FIDELITY_TARGET;
+  }
+  const int64_t tiles = (int64_t)((max_len + 127) / 128) * num_q_heads * n_prompts;
+  if (tiles > 0x7FFFFFFFLL) return fail(EKV_ERR_UNSUPPORTED, "launch grid too large");
+  ekv::PrefillParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_rows = q_rows;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.n_prompts = n_prompts;
+  p.max_len = max_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = kv->num_kv_heads;
+  p.head_dim = kv->head_dim;
+  p.causal = causal;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.out = out;
+  p.out_f32 = out_dtype == EKV_F32;
+  p.lse = lse;
+  p.page_table = page_table;
+  p.pt_stride = pt_stride;
+  p.fidelity = fidelity;
+  p.uniform_kind = uniform_kind;
+  p.k_target = static_cast<const uint16_t*>(kv->k_target);
+  p.v_target = static_cast<const uint16_t*>(kv->v_target);
+  p.n_target = kv->n_target_pages;
+  p.k_compact = static_cast<const uint16_t*>(kv->k_compact);
+  p.v_compact = kv->v_compact;
+  p.v_scale = kv->v_scale;
+  p.n_compact = kv->n_compact_pages;
+  return hip_status(ekv::launch_prefill(p, static_cast<hipStream_t>(stream)), "paged prefill launch");
+}
+
 ekv_status ekv_append_tokens(const ekv_paged_kv* kv, const void* k_new, const void* v_new,
                              const int32_t* slot_mapping, int32_t n_tokens, void* stream) {
   if (!kv) return fail(EKV_ERR_INVALID_ARG, "kv descriptor is NULL");

@@ -59,6 +59,19 @@ struct PrefillParams {
   void* out;
   int32_t out_f32;
   float* lse;
+  // Paged source (direct route): keys/values of prompt p come from its row of
+  // page_table through the pools below; k, v, kv_start are unused then.
+  const int32_t* page_table;  // [n_prompts][pt_stride]; NULL = workspace rows
+  int32_t pt_stride;
+  const uint8_t* fidelity;    // NULL: every page has kind uniform_kind
+  int32_t uniform_kind;
+  const uint16_t* k_target;
+  const uint16_t* v_target;
+  int32_t n_target;
+  const uint16_t* k_compact;
+  const uint8_t* v_compact;
+  const float* v_scale;
+  int32_t n_compact;
 };
 
 struct AppendParams {

@@ -24,6 +24,20 @@
 // with its own L2) walks a contiguous range of (prompt, head, row tile), so
 // the K/V rows a head reuses stay in one L2; within a head the longest
 // (last) causal row tiles start first.
+//
+// Two sources of K/V, one compute loop:
+//   workspace rows  the gather route: contiguous FP16 rows per prompt;
+//   pages           the direct route ("Memory-Traffic Saturation ...",
+//                   section "Existing fallback: mixed-type prefill"; ElasticKV
+//                   section 3.2): the prompt's own page-table row, TARGET pages
+//                   as stored, compact pages' E4M3 values expanded while the
+//                   tile is staged, with the scaled gather's rounding
+//                   (fp16(fp32(e4m3) * fp32(scale))), so both routes feed the
+//                   MFMAs identical operands.
+// A 64-key tile is 4 pages.  In the paged source each K chunk a thread loads
+// lies in a page that is uniform across its wavefront, and (head dim 128)
+// each wavefront stages the V of one page, so every load goes through a
+// per-page buffer descriptor in scalar registers.
 #include "ekv_device.hpp"
 #include "ekv_internal.hpp"
 
@@ -36,6 +50,7 @@ constexpr int kThreads = 256;
 constexpr float kTau = 8.0f;
 constexpr float kNegBig = -1.0e30f;
 constexpr int kXcds = 8;
+constexpr int kMaxPromptPages = 512;  // paged source: prompts of at most 8192 tokens
 
 template <int D>
 struct Smem {
@@ -45,6 +60,18 @@ struct Smem {
   f16 vt[D * vStride];
 };
 
+// V^T column swizzle of the paged source: the 8-byte key quad kq of V^T row
+// d is stored at quad kq ^ ((d / 32) & 3).  There a wavefront stages the four
+// key quads of one page for all 16 d-octets, and the plain layout would put
+// those stores on a quarter of the LDS banks; the swizzle spreads them and
+// keeps the MFMA reads conflict-free.  The workspace source stages sixteen
+// key quads per wavefront and is faster unswizzled.  The value depends on d / 8
+// only: one per staging thread (rows 8 oc .. 8 oc + 7) and per MFMA read.
+template <bool SWZ>
+__device__ __forceinline__ int vt_swz(int d) {
+  return SWZ ? (d >> 5) & 3 : 0;
+}
+
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -53,8 +80,30 @@ template <int D>
 struct TileRegs {
   static constexpr int KCH = kN * D / 8 / kThreads;  // 16-byte K chunks per thread
   uint4 k[KCH];
-  uint4 v[4];  // 4 key rows x 8 d of one (key quad, d octet) unit
+  uint2 vlo[4];  // 4 key rows x 8 d of one (key quad, d octet) unit: d 0..3 of
+  uint2 vhi[4];  // each row in vlo, d 4..7 in vhi; for a compact page (paged
+                 // source) vlo holds the row's 8 E4M3 codes and vhi is unused
+  float vscale;
+  bool v_codes;
 };
+
+// fp32 -> fp16 pair, round to nearest even each.
+__device__ __forceinline__ uint32_t pack_rne(float a, float b) {
+  f16x2 r;
+  r.x = (f16)a;
+  r.y = (f16)b;
+  return bits(r);
+}
+
+// Eight E4M3 codes -> eight fp16 values fp16(fp32(code) * s): the code is
+// exact in fp32, one fp32 multiply (round to nearest even), one fp16 rounding.
+__device__ __forceinline__ uint4 expand8(uint2 w, float s) {
+#pragma clang fp contract(off)
+  const f32x2 a = e4m3x2_f32(w.x, false), b = e4m3x2_f32(w.x, true);
+  const f32x2 c = e4m3x2_f32(w.y, false), d = e4m3x2_f32(w.y, true);
+  return make_uint4(pack_rne(a.x * s, a.y * s), pack_rne(b.x * s, b.y * s),
+                    pack_rne(c.x * s, c.y * s), pack_rne(d.x * s, d.y * s));
+}
 
 // Tile loads are buffer loads through per-prompt descriptors (SGPRs) whose
 // range ends at the prompt's last key row of this KV head, so rows past the
@@ -72,12 +121,17 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, __amdgpu_buffer_rsrc_t
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], tile_off, 0);
-    r.v[i] = make_uint4(x.x, x.y, x.z, x.w);
+    r.vlo[i] = make_uint2(x.x, x.y);
+    r.vhi[i] = make_uint2(x.z, x.w);
   }
+  r.v_codes = false;
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(Smem<D>& s, const TileRegs<D>& r) {
+// Writes the staged tile to LDS: K row-major, V transposed.  The V unit
+// (key quad kq, d octet oc) of this thread holds keys 4kq..4kq+3, d 8oc..8oc+7.
+template <int D, bool SWZ>
+__device__ __forceinline__ void store_tile(Smem<D>& s, TileRegs<D>& r, int kq, int oc, bool v_active,
+                                           int valid_keys) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::KCH; ++i) {
@@ -85,30 +139,210 @@ __device__ __forceinline__ void store_tile(Smem<D>& s, const TileRegs<D>& r) {
     const int key = idx / (D / 8), ch = idx % (D / 8);
     *reinterpret_cast<uint4*>(&s.k[key * Smem<D>::kStride + 8 * ch]) = r.k[i];
   }
-  constexpr int units = (kN / 4) * (D / 8);
-  if (t < units) {
-    const int kq = t % (kN / 4), oc = t / (kN / 4);
-    const uint32_t r0[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
-    const uint32_t r1[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
-    const uint32_t r2[4] = {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w};
-    const uint32_t r3[4] = {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
+  if (v_active) {
+    uint4 v[4];
+    // head dim 128: the page kind is wave-uniform (a branch); head dim 64: the
+    // two half-wavefronts may hold different pages (a select)
+    const bool codes = D == 128 ? (bool)__builtin_amdgcn_readfirstlane((int)r.v_codes) : r.v_codes;
+    if (codes) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = expand8(r.vlo[i], r.vscale);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = make_uint4(r.vlo[i].x, r.vlo[i].y, r.vhi[i].x, r.vhi[i].y);
+    }
+    if (valid_keys < kN) {  // last tile of a prompt: value rows past its end are zero
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * kq + i >= valid_keys) v[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    const uint32_t r0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+    const uint32_t r1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+    const uint32_t r2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
+    const uint32_t r3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       // d = 8*oc + 2w and 2w+1: four keys' values, key order 4kq..4kq+3
       const uint2 even = make_uint2(perm(r1[w], r0[w], 0x05040100u), perm(r3[w], r2[w], 0x05040100u));
       const uint2 odd = make_uint2(perm(r1[w], r0[w], 0x07060302u), perm(r3[w], r2[w], 0x07060302u));
       const int d = 8 * oc + 2 * w;
-      *reinterpret_cast<uint2*>(&s.vt[d * Smem<D>::vStride + 4 * kq]) = even;
-      *reinterpret_cast<uint2*>(&s.vt[(d + 1) * Smem<D>::vStride + 4 * kq]) = odd;
+      const int kqs = kq ^ vt_swz<SWZ>(8 * oc);
+      *reinterpret_cast<uint2*>(&s.vt[d * Smem<D>::vStride + 4 * kqs]) = even;
+      *reinterpret_cast<uint2*>(&s.vt[(d + 1) * Smem<D>::vStride + 4 * kqs]) = odd;
     }
   }
 }
 
+// Paged source: per-workgroup pool bases (already offset to KV head g) and row sizes.
+struct PagedSrc {
+  const char* kt;
+  const char* vt;
+  const char* kc;
+  const char* vc;
+  uint32_t rowb;     // bytes per fp16 token row (all KV heads)
+  uint32_t rowb8;    // bytes per E4M3 token row
+  uint32_t range16;  // descriptor range of one head's fp16 page: 15 rows + D halves
+  uint32_t range8;   // the same for an E4M3 page
+};
+
+// Metadata of the 4 pages of one tile: meta = (phys << 1) | kind, or < 0 for
+// a page past the prompt; the scale of a compact page.  Read from LDS one
+// tile ahead of its use (two 16-byte reads) and made wave-uniform only where
+// it is used, so the LDS latency never stalls the load issue.
+struct TileMetaRaw {
+  int4 m;
+  float4 s;
+};
+struct TileMeta {
+  int m[4];
+  float s[4];
+};
+
+__device__ __forceinline__ TileMetaRaw read_tile_meta(const int* s_meta, const float* s_scale, int it) {
+  return TileMetaRaw{*reinterpret_cast<const int4*>(s_meta + 4 * it),
+                     *reinterpret_cast<const float4*>(s_scale + 4 * it)};
+}
+
+__device__ __forceinline__ float rfl(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ TileMeta uniform_meta(const TileMetaRaw& r) {
+  TileMeta t;
+  t.m[0] = __builtin_amdgcn_readfirstlane(r.m.x);
+  t.m[1] = __builtin_amdgcn_readfirstlane(r.m.y);
+  t.m[2] = __builtin_amdgcn_readfirstlane(r.m.z);
+  t.m[3] = __builtin_amdgcn_readfirstlane(r.m.w);
+  t.s[0] = rfl(r.s.x);
+  t.s[1] = rfl(r.s.y);
+  t.s[2] = rfl(r.s.z);
+  t.s[3] = rfl(r.s.w);
+  return t;
+}
+
+// Entry k of the tile metadata for a wave-uniform runtime k (selects, so the
+// arrays stay in registers).
+__device__ __forceinline__ int tm_meta(const TileMeta& t, int k) {
+  return k == 0 ? t.m[0] : k == 1 ? t.m[1] : k == 2 ? t.m[2] : t.m[3];
+}
+__device__ __forceinline__ float tm_scale(const TileMeta& t, int k) {
+  return k == 0 ? t.s[0] : k == 1 ? t.s[1] : k == 2 ? t.s[2] : t.s[3];
+}
+
+// Descriptors of one page (meta = (phys << 1) | kind, always a valid page:
+// pages past the prompt were staged as a copy of its page 0).  Each range is
+// one head's page; rows past the prompt end are masked (K) or zeroed (V) in
+// the tile instead.  V keeps its base and the code flag: the loads build the
+// descriptors of its two row halves.
+struct PageDesc {
+  __amdgpu_buffer_rsrc_t k;
+  const char* vbase;
+  float scale;
+  bool codes;
+};
+
+__device__ __forceinline__ PageDesc page_desc(PagedSrc src, int meta, float scale) {
+  PageDesc pd;
+  const int64_t phys = meta >> 1;
+  pd.codes = meta & 1;
+  const int64_t off16 = phys * kPage * src.rowb;
+  pd.k = __builtin_amdgcn_make_buffer_rsrc((void*)((pd.codes ? src.kc : src.kt) + off16), (short)0,
+                                           src.range16, kBufferFlags);
+  pd.vbase = pd.codes ? src.vc + phys * kPage * src.rowb8 : src.vt + off16;
+  pd.scale = scale;
+  return pd;
+}
+
+// V rows 4(kq%4) .. +3 of one page for this thread's unit, each as two 8-byte
+// halves.  The same eight loads serve both kinds, so both write the same
+// registers and no wait or spill follows from the kind: an fp16 page gives
+// d 0..3 and d 4..7; a compact page gives its 8 codes in the low half while
+// the high half reads through a zero-range descriptor (no memory access).
+__device__ __forceinline__ void load_v_page(uint2* lo, uint2* hi, const PageDesc& pd, const PagedSrc& src,
+                                            uint32_t voff16, uint32_t voff8) {
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)pd.vbase, (short)0, pd.codes ? src.range8 : src.range16, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)pd.vbase, (short)0, pd.codes ? 0u : src.range16, kBufferFlags);
+  const uint32_t off = pd.codes ? voff8 : voff16;
+  const uint32_t stride = pd.codes ? src.rowb8 : src.rowb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(vr, off, i * stride, 0);
+    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(hr, voff16 + 8u, i * src.rowb, 0);
+    lo[i] = make_uint2(a.x, a.y);
+    hi[i] = make_uint2(b.x, b.y);
+  }
+}
+
+// Loads tile `it` (keys 64 it .. 64 it + 63 = prompt pages 4 it .. 4 it + 3).
+// K chunk i of this thread lies in tile page D == 128 ? i : 2 i + wave / 2;
+// the V unit's page is the wavefront (D 128) or the half-wavefront (D 64).
 template <int D>
+__device__ __forceinline__ void load_tile_paged(TileRegs<D>& r, PagedSrc src, const TileMetaRaw& raw, int it,
+                                                int wave, int lane, uint32_t koff, uint32_t voff16,
+                                                uint32_t voff8) {
+  const TileMeta tm = uniform_meta(raw);
+  if constexpr (D == 128) {
+#pragma unroll
+    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+      const PageDesc pd = page_desc(src, tm.m[i], tm.s[i]);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pd.k, koff, 0, 0);
+      r.k[i] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+  } else {  // chunk i lies in page 2i + wave/2: a choice of two
+    const bool hi = wave >> 1;
+#pragma unroll
+    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+      const PageDesc pd = page_desc(src, hi ? tm.m[2 * i + 1] : tm.m[2 * i], hi ? tm.s[2 * i + 1] : tm.s[2 * i]);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pd.k, koff, 0, 0);
+      r.k[i] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+  }
+  if constexpr (D == 128) {
+    const PageDesc pd = page_desc(src, tm_meta(tm, wave), tm_scale(tm, wave));
+    load_v_page(r.vlo, r.vhi, pd, src, voff16, voff8);
+    r.v_codes = pd.codes;
+    r.vscale = pd.scale;
+  } else if (wave < 2) {  // D 64: 128 V units, two pages per wavefront
+    const bool w1 = wave == 1;
+    const PageDesc pa = page_desc(src, w1 ? tm.m[2] : tm.m[0], w1 ? tm.s[2] : tm.s[0]);
+    const PageDesc pb = page_desc(src, w1 ? tm.m[3] : tm.m[1], w1 ? tm.s[3] : tm.s[1]);
+    if (lane < 32) {
+      load_v_page(r.vlo, r.vhi, pa, src, voff16, voff8);
+      r.v_codes = pa.codes;
+      r.vscale = pa.scale;
+    } else {
+      load_v_page(r.vlo, r.vhi, pb, src, voff16, voff8);
+      r.v_codes = pb.codes;
+      r.vscale = pb.scale;
+    }
+  }
+}
+
+// Writes NaN to output rows [r_lo, r_hi) of head h (and their LSE).
+template <int D>
+__device__ void write_nan_rows(const PrefillParams& p, int64_t q0, int r_lo, int r_hi, int h) {
+  const float qnan = __builtin_nanf("");
+  const int64_t hq_row = (int64_t)p.num_q_heads * D;
+  for (int64_t i = threadIdx.x; i < (int64_t)(r_hi - r_lo) * D; i += kThreads) {
+    const int64_t rr = r_lo + i / D;
+    const int64_t o = (q0 + rr) * hq_row + (int64_t)h * D + i % D;
+    if (p.out_f32) static_cast<float*>(p.out)[o] = qnan;
+    else static_cast<f16*>(p.out)[o] = (f16)qnan;
+    if (p.lse && i % D == 0) p.lse[(q0 + rr) * p.num_q_heads + h] = qnan;
+  }
+}
+
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, int n_mtiles) {
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   __shared__ Smem<D> sbuf[2];  // double buffer: tile i computes from one while i+1 is stored
+  // paged source: the prompt's page metadata for the tiles this workgroup reads
+  __shared__ __attribute__((aligned(16))) int s_meta[PAGED ? kMaxPromptPages : 4];
+  __shared__ __attribute__((aligned(16))) float s_scale[PAGED ? kMaxPromptPages : 4];
+  __shared__ int s_bad;
 
   // XCD-aware work mapping (see header).
   const int total = (int)(gridDim.x);
@@ -126,8 +360,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   if (q0 < 0 || q1 < q0 || q1 > p.q_rows) return;  // rows not addressable: nothing to write
   const int L = q1 - q0;
   const int m0 = mt * kM;
-  const int kv0 = p.kv_start[prompt];
-  const bool ok = L <= p.max_len && kv0 >= 0 && (int64_t)kv0 + L <= p.kv_rows;
+  const int kv0 = PAGED ? 0 : p.kv_start[prompt];
+  const bool ok = PAGED ? (L <= p.max_len && L <= kMaxPromptPages * kPage &&
+                           (int64_t)L <= (int64_t)p.pt_stride * kPage)
+                        : (L <= p.max_len && kv0 >= 0 && (int64_t)kv0 + L <= p.kv_rows);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -137,19 +373,63 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   const int64_t hq_row = (int64_t)p.num_q_heads * D;
 
   if (!ok) {  // offsets outside the buffers or an over-long prompt: row tile 0 writes NaN rows
-    if (mt != 0) return;
-    const float qnan = __builtin_nanf("");
-    for (int64_t i = threadIdx.x; i < (int64_t)L * D; i += kThreads) {
-      const int64_t rr = i / D;
-      const int64_t o = ((int64_t)q0 + rr) * hq_row + (int64_t)h * D + i % D;
-      if (p.out_f32) static_cast<float*>(p.out)[o] = qnan;
-      else static_cast<f16*>(p.out)[o] = (f16)qnan;
-      if (p.lse && i % D == 0) p.lse[((int64_t)q0 + rr) * p.num_q_heads + h] = qnan;
-    }
+    if (mt == 0) write_nan_rows<D>(p, q0, 0, L, h);
     return;
   }
 
   if (m0 >= L) return;
+
+  const int n_end = p.causal ? min(L, m0 + kM) : L;
+  const int n_tiles = (n_end + kN - 1) / kN;
+  const uint32_t rowb = (uint32_t)p.num_kv_heads * D * 2u;  // bytes per key row
+
+  PagedSrc src{};
+  if constexpr (PAGED) {
+    // stage page ids, kinds and scales of pages 0 .. 4 n_tiles - 1; a page
+    // past the prompt gets -2 (reads zeros); an out-of-pool id or unknown flag
+    // marks the row tile bad (its rows are written as NaN)
+    if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
+    const int64_t pt_row = (int64_t)prompt * p.pt_stride;
+    for (int j = threadIdx.x; j < 4 * n_tiles; j += kThreads) {
+      int meta = -2;
+      float sc = 1.0f;
+      if (kPage * j < L) {
+        const int id = p.page_table[pt_row + j];
+        const int kind = p.fidelity ? (int)p.fidelity[pt_row + j] : p.uniform_kind;
+        const int n_pool = kind == 1 ? p.n_compact : p.n_target;
+        if ((kind == 0 || kind == 1) && id >= 0 && id < n_pool) {
+          meta = (id << 1) | kind;
+          if (kind == 1) sc = p.v_scale[(int64_t)id * p.num_kv_heads + g];
+        } else {
+          s_bad = 1;
+        }
+      }
+      s_meta[j] = meta;
+      s_scale[j] = sc;
+    }
+    __syncthreads();
+    if (s_bad) {
+      write_nan_rows<D>(p, q0, m0, min(L, m0 + kM), h);
+      return;
+    }
+    // pages past the prompt: a copy of page 0 (in bounds; their keys are masked
+    // and their values zeroed in the tile)
+    for (int j = threadIdx.x; j < 4 * n_tiles; j += kThreads)
+      if (kPage * j >= L) {
+        s_meta[j] = s_meta[0];
+        s_scale[j] = s_scale[0];
+      }
+    __syncthreads();
+    src.kt = reinterpret_cast<const char*>(p.k_target) + (int64_t)g * D * 2;
+    src.vt = reinterpret_cast<const char*>(p.v_target) + (int64_t)g * D * 2;
+    src.kc = reinterpret_cast<const char*>(p.k_compact) + (int64_t)g * D * 2;
+    src.vc = reinterpret_cast<const char*>(p.v_compact) + (int64_t)g * D;
+    src.rowb = rowb;
+    src.rowb8 = (uint32_t)p.num_kv_heads * D;
+    src.range16 = (kPage - 1) * rowb + 2u * D;
+    src.range8 = (kPage - 1) * src.rowb8 + (uint32_t)D;
+  }
 
   // Q^T operand: lane holds Q[qpos][16ks + 8half .. +8] for each k-step.
   f16x8 qb[KS];
@@ -168,38 +448,65 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m = kNegBig, l = 0.f;
 
-  const int n_end = p.causal ? min(L, m0 + kM) : L;
-  const int n_tiles = (n_end + kN - 1) / kN;
-  // buffer descriptors over this prompt's K/V rows of KV head g
-  const uint32_t rowb = (uint32_t)p.num_kv_heads * D * 2u;  // bytes per key row
-  const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2u;
-  const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
-  const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
-  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, span, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, span, kBufferFlags);
+  // Per-lane load offsets.  V unit (kq, oc): workspace source kq = t % 16
+  // (consecutive lanes take consecutive key quads); paged source kq = t / (D/8),
+  // so a wavefront's units share one page (D 128) or two (D 64).
+  constexpr int units = (kN / 4) * (D / 8);
+  const bool v_active = threadIdx.x < units;
+  const int vt_id = v_active ? threadIdx.x : 0;
+  const int kq = PAGED ? vt_id / (D / 8) : vt_id % (kN / 4);
+  const int oc = PAGED ? vt_id % (D / 8) : vt_id / (kN / 4);
+  __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, kBufferFlags);
+  __amdgpu_buffer_rsrc_t vr = kr;
   uint32_t koff[TileRegs<D>::KCH], voff[4];
+  uint32_t pkoff = 0, pvoff16 = 0, pvoff8 = 0;
+  if constexpr (PAGED) {
+    // K chunk i: key t/(D/8) + (256/(D/8)) i, i.e. the same slot of tile page
+    // D == 128 ? i : 2i + wave/2; V rows 4(kq%4) .. +3 of tile page kq/4
+    pkoff = (uint32_t)((threadIdx.x / (D / 8)) % kPage) * rowb + 16u * (threadIdx.x % (D / 8));
+    pvoff16 = (uint32_t)(4 * (kq % 4)) * rowb + 16u * oc;
+    pvoff8 = (uint32_t)(4 * (kq % 4)) * src.rowb8 + 8u * oc;
+  } else {
+    // workspace source: buffer descriptors over this prompt's K/V rows of KV head g
+    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2u;
+    const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
+    const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
+    kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, span, kBufferFlags);
+    vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, span, kBufferFlags);
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
-    const int idx = threadIdx.x + kThreads * i;
-    koff[i] = (uint32_t)(idx / (D / 8)) * rowb + 16u * (idx % (D / 8));
-  }
-  {
-    constexpr int units = (kN / 4) * (D / 8);
-    const int t = threadIdx.x < units ? threadIdx.x : 0;
-    const int kq = t % (kN / 4), oc = t / (kN / 4);
+    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+      const int idx = threadIdx.x + kThreads * i;
+      koff[i] = (uint32_t)(idx / (D / 8)) * rowb + 16u * (idx % (D / 8));
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)(4 * kq + i) * rowb + 16u * oc;
   }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   TileRegs<D> tr;
-  load_tile<D>(tr, kr, vr, koff, voff, 0u);
-  store_tile<D>(sbuf[0], tr);
+  tr.v_codes = false;
+  tr.vscale = 1.0f;
+  // paged source: metadata of the tile whose loads are issued next, read
+  // from LDS one iteration ahead
+  TileMetaRaw tmeta{};
+  if constexpr (PAGED) tmeta = read_tile_meta(s_meta, s_scale, 0);
+#define EKV_ISSUE_TILE(IT)                                                                      \
+  do {                                                                                          \
+    if constexpr (PAGED) {                                                                      \
+      load_tile_paged<D>(tr, src, tmeta, (IT), wave_u, lane, pkoff, pvoff16, pvoff8);           \
+      if ((IT) + 1 < n_tiles) tmeta = read_tile_meta(s_meta, s_scale, (IT) + 1);                \
+    } else {                                                                                    \
+      load_tile<D>(tr, kr, vr, koff, voff, (uint32_t)((IT) * kN) * rowb);                       \
+    }                                                                                           \
+  } while (0)
+  EKV_ISSUE_TILE(0);
+  store_tile<D, PAGED>(sbuf[0], tr, kq, oc, v_active, PAGED ? L : kN);
   __syncthreads();
 
   for (int it = 0; it < n_tiles; ++it) {
     const int n0 = it * kN;
     Smem<D>& s = sbuf[it & 1];
     // the next tile's loads are in flight while this tile computes
-    if (it + 1 < n_tiles) load_tile<D>(tr, kr, vr, koff, voff, (uint32_t)(n0 + kN) * rowb);
+    if (it + 1 < n_tiles) EKV_ISSUE_TILE(it + 1);
 
     if (!(p.causal && n0 > r0 + 31)) {  // skip tiles whose keys all follow this wavefront's rows
 
@@ -259,11 +566,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
     // O^T += V^T . P^T
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const f16* vp = &s.vt[(32 * db + col) * Smem<D>::vStride + 4 * half];
+      const f16* vp = &s.vt[(32 * db + col) * Smem<D>::vStride];
+      const int sw = vt_swz<PAGED>(32 * db + col);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp + 16 * kk);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16 * kk + 8);
+        // key quads half + 4 kk (keys 16 kk + 4 half ..) and half + 4 kk + 2
+        const uint2 lo = *reinterpret_cast<const uint2*>(vp + 4 * ((half + 4 * kk) ^ sw));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 4 * ((half + 4 * kk + 2) ^ sw));
         const uint4 a4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
         oacc[db] = mfma32(__builtin_bit_cast(f16x8, a4), pb[kk], oacc[db]);
       }
@@ -271,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
     }
     // store the next tile into the other buffer; one barrier publishes it and
     // guarantees every wavefront has finished reading the buffer it overwrites next
-    if (it + 1 < n_tiles) store_tile<D>(sbuf[(it + 1) & 1], tr);
+    if (it + 1 < n_tiles) store_tile<D, PAGED>(sbuf[(it + 1) & 1], tr, kq, oc, v_active, PAGED ? L - n0 - kN : kN);
     __syncthreads();
   }
 
@@ -299,18 +608,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   if (p.lse && half == 0) p.lse[qrow * p.num_q_heads + h] = (m + log2f(l)) * kLn2;
 }
 
+#undef EKV_ISSUE_TILE
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (p.n_prompts == 0 || p.max_len == 0) return hipSuccess;
   const int n_mtiles = (p.max_len + kM - 1) / kM;
   const int64_t blocks = (int64_t)n_mtiles * p.num_q_heads * p.n_prompts;
-  if (p.head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, n_mtiles);
-  else if (p.head_dim == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, n_mtiles);
-  else
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  const bool paged = p.page_table != nullptr;
+  if (paged && p.max_len > kMaxPromptPages * kPage) return hipErrorInvalidValue;
+  if (p.head_dim == 128) {
+    if (paged) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, p, n_mtiles);
+    else hipLaunchKernelGGL((prefill_kernel<128, false>), grid, block, 0, stream, p, n_mtiles);
+  } else if (p.head_dim == 64) {
+    if (paged) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, block, 0, stream, p, n_mtiles);
+    else hipLaunchKernelGGL((prefill_kernel<64, false>), grid, block, 0, stream, p, n_mtiles);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ EXPORTED = (
     "ekv_abi_version", "ekv_status_string", "ekv_last_error", "ekv_decode_pages_per_split",
     "ekv_decode_plan_pages_per_split",
     "ekv_decode_scratch_bytes", "ekv_decode_attention", "ekv_gather_compact_pages",
-    "ekv_prefill_attention", "ekv_append_tokens", "ekv_quantize_pages", "ekv_e4m3_to_f16",
+    "ekv_prefill_attention", "ekv_prefill_paged_attention", "ekv_append_tokens", "ekv_quantize_pages", "ekv_e4m3_to_f16",
 )
 
 
@@ -71,6 +71,10 @@ _lib.ekv_prefill_attention.restype = ctypes.c_int
 _lib.ekv_prefill_attention.argtypes = [
     _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, ctypes.c_int,
     _vp, _vp]
+_lib.ekv_prefill_paged_attention.restype = ctypes.c_int
+_lib.ekv_prefill_paged_attention.argtypes = [
+    ctypes.POINTER(PagedKV), _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _f32, _vp,
+    ctypes.c_int, _vp, _vp]
 _lib.ekv_append_tokens.restype = ctypes.c_int
 _lib.ekv_append_tokens.argtypes = [ctypes.POINTER(PagedKV), _vp, _vp, _vp, _i32, _vp]
 _lib.ekv_quantize_pages.restype = ctypes.c_int
@@ -199,6 +203,20 @@ def ekv_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _ptr(q), q_rows, _ptr(k), _ptr(v), kv_rows, _ptr(cu_seqlens_q), _ptr(kv_start),
         int(kv_start.shape[0]), int(max_len), hq, hkv, d, 1 if causal else 0, float(sm_scale),
         _ptr(out), _dtype_code(out), _ptr(lse), _stream(stream)))
+
+
+def ekv_prefill_paged_attention(kv: PagedKV, q: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                                page_table: torch.Tensor, fidelity: Optional[torch.Tensor], max_len: int,
+                                sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                                causal: bool = True, stream=None) -> None:
+    """Causal FP16 prefill straight from each prompt's pages (see ekv.h).
+
+    q: [T, Hq, D]; page_table: [n_prompts, stride] int32; fidelity: same shape uint8 or None."""
+    q_rows, hq, _ = q.shape
+    _check(_lib.ekv_prefill_paged_attention(
+        ctypes.byref(kv), _ptr(q), q_rows, _ptr(cu_seqlens_q), _ptr(page_table),
+        int(page_table.shape[1]), _ptr(fidelity), int(page_table.shape[0]), int(max_len), hq,
+        1 if causal else 0, float(sm_scale), _ptr(out), _dtype_code(out), _ptr(lse), _stream(stream)))
 
 
 def ekv_append_tokens(kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor,

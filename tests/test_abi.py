@@ -22,7 +22,7 @@ def _declared():
 
 def test_every_declared_function_is_exported():
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(ekv._lib, n), n
     assert sorted(ekv.EXPORTED) == names
@@ -160,3 +160,22 @@ def test_quantize_validation():
     assert f(ctypes.byref(kv), FAKE, FAKE, -1, FAKE, None, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
     assert f(ctypes.byref(_kv(d=32)), FAKE, FAKE, 64, FAKE, None, FAKE, 4, None) == ekv.EKV_ERR_UNSUPPORTED
     assert f(ctypes.byref(kv), FAKE, FAKE, 64, FAKE, None, FAKE, 0, None) == ekv.EKV_OK
+
+
+def _paged_prefill(kv, max_len=8192, hq=32, causal=1, out=FAKE, pt_stride=512, fidelity=FAKE):
+    return ekv._lib.ekv_prefill_paged_attention(ctypes.byref(kv) if kv is not None else None, FAKE, 1000,
+                                                FAKE, FAKE, pt_stride, fidelity, 2, max_len, hq, causal,
+                                                0.088, out, 0, None, None)
+
+
+def test_paged_prefill_validation():
+    kv = _kv()
+    assert _paged_prefill(kv, max_len=8193, pt_stride=600) == ekv.EKV_ERR_NOT_ELIGIBLE
+    assert _paged_prefill(kv, hq=33) == ekv.EKV_ERR_INVALID_ARG
+    assert _paged_prefill(_kv(d=80)) == ekv.EKV_ERR_UNSUPPORTED
+    assert _paged_prefill(kv, causal=2) == ekv.EKV_ERR_INVALID_ARG
+    assert _paged_prefill(kv, out=None) == ekv.EKV_ERR_INVALID_ARG
+    assert _paged_prefill(kv, pt_stride=100) == ekv.EKV_ERR_INVALID_ARG
+    assert _paged_prefill(_kv(n_t=5, n_c=5), fidelity=None) == ekv.EKV_ERR_INVALID_ARG
+    assert _paged_prefill(None) == ekv.EKV_ERR_INVALID_ARG
+    assert _paged_prefill(kv, max_len=0) == ekv.EKV_OK

@@ -159,3 +159,49 @@ def test_writer_quantizes_32x8192_prompts_into_16384_pages():
     assert np.array_equal(got_k.view(np.uint16), K.view(np.uint16))
     assert np.array_equal(got_v, V)
     assert np.array_equal(got_s.view(np.uint32), S.view(np.uint32))
+
+
+def test_paged_prefill_32x8192_one_launch():
+    """Direct paged prefill of all 32 prompts in one launch (the bench's call): sampled rows
+    against the oracle, and the first 8 prompts bit-equal to the gather route's chunk."""
+    step("fullsize paged prefill 32 x 8192, one launch")
+    pc = synth.compact_prefill_case(seed=4)
+    c = pc.paged
+    dc = DeviceCase(c)
+    H, D, Hq = c.num_kv_heads, c.head_dim, c.num_q_heads
+    T = int(pc.cu_seqlens_q[-1])
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    ekv().ekv_prefill_paged_attention(dc.kv(), dc.q, dev(pc.cu_seqlens_q), dc.page_table, None, 8192,
+                                      c.sm_scale, out, lse)
+    torch.cuda.synchronize()
+    step("gather route, chunk 0, for bit comparison")
+    prompts = list(range(8))
+    ids, kv_start = pc.chunk_pages(prompts)
+    ws_k = torch.empty((4096, 16, H, D), dtype=torch.float16, device="cuda")
+    ws_v = torch.empty_like(ws_k)
+    ekv().ekv_gather_compact_pages(dc.kv(), dev(ids), True, ws_k, ws_v)
+    r1 = int(pc.cu_seqlens_q[8])
+    g_out = torch.empty((r1, Hq, D), dtype=torch.float32, device="cuda")
+    g_lse = torch.empty((r1, Hq), dtype=torch.float32, device="cuda")
+    ekv().ekv_prefill_attention(dc.q[:r1], ws_k, ws_v, dev(pc.cu_seqlens_q[:9]), dev(kv_start), 8192,
+                                c.sm_scale, g_out, g_lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:r1].view(torch.int32), g_out.view(torch.int32))
+    assert torch.equal(lse[:r1].view(torch.int32), g_lse.view(torch.int32))
+    del g_out, g_lse, ws_k, ws_v
+    rng = np.random.default_rng(47)
+    checked = [0, 9, 17, 31]
+    local = [np.array(_sample_rows(8192, rng)) for _ in checked]
+    sample = np.concatenate([int(pc.cu_seqlens_q[p]) + r for p, r in zip(checked, local)])
+    got = out[dev(sample).long()].cpu().numpy()
+    glse = lse[dev(sample).long()].cpu().numpy()
+    # the oracle over just the checked prompts (their rows, pages and flags)
+    q_sub = np.concatenate([c.q[pc.cu_seqlens_q[p]:pc.cu_seqlens_q[p + 1]] for p in checked])
+    cu_sub = np.arange(len(checked) + 1, dtype=np.int32) * 8192
+    rows_sub = np.concatenate([i * 8192 + r for i, r in enumerate(local)])
+    want, wlse = oracle.paged_prefill_attention(q_sub, c.k_target, c.v_target, c.k_compact, c.v_compact,
+                                                c.v_scale, c.page_table[checked], c.fidelity[checked],
+                                                cu_sub, True, c.sm_scale, rows=rows_sub)
+    assert_close(got, want[rows_sub], what="paged prefill rows")
+    assert_lse_close(glse, wlse[rows_sub])

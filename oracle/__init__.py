@@ -24,6 +24,7 @@ scaled_dot_product_attention in float64) and invariants.  No function here
 is "parity unpinned".
 """
 from .e4m3 import E4M3FN_TABLE, e4m3fn_value, decode_e4m3fn
+from .base import base_page, base_values, high_bytes, pack_base_pairs
 from .paged import sequence_kv
 from .attention import attention_rows, decode_attention, prefill_attention
 from .gather import gather_compact_pages
@@ -35,4 +36,5 @@ __all__ = [
     "attention_rows", "decode_attention", "prefill_attention",
     "gather_compact_pages", "append_tokens", "quantize_page", "quantize_pages",
     "encode_e4m3fn", "encode_e4m3fn_array", "paged_prefill_attention", "prompt_rows",
+    "base_page", "base_values", "high_bytes", "pack_base_pairs",
 ]

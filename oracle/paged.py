@@ -8,17 +8,21 @@ page has a fidelity mode and pages of both modes are read in one batch.
 FP16 keys, E4M3 values, value scales applied in attention.
 
 Readings taken where the pages are silent: the fidelity flag is one uint8 per
-page-table entry (0 = TARGET, 1 = COMPACT); the page id indexes the pool the
-flag selects; the value scale is fp32 per (compact page, KV head); token t of
-sequence b lives in logical page t // 16, slot t % 16; only t < len_b is read.
+page-table entry (0 = TARGET, 1 = COMPACT, 2 = ElasticKV BASE); the page id
+indexes the pool the flag selects (a BASE id b names half b % 2 of TARGET
+block b // 2, see ``base.py``); the value scale is fp32 per (compact page, KV
+head); token t of sequence b lives in logical page t // 16, slot t % 16; only
+t < len_b is read.
 """
 import numpy as np
 
+from .base import base_page, base_values
 from .e4m3 import decode_e4m3fn
 
 PAGE = 16
 TARGET = 0
 COMPACT = 1
+BASE = 2
 
 
 def sequence_kv(k_target, v_target, k_compact, v_compact, v_scale,
@@ -45,6 +49,9 @@ def sequence_kv(k_target, v_target, k_compact, v_compact, v_scale,
             K[t:t + n] = k_compact[phys, :n].astype(np.float64)
             V[t:t + n] = decode_e4m3fn(v_compact[phys, :n]) * \
                 v_scale[phys].astype(np.float64)[None, :, None]
+        elif flag == BASE:   # [ekv] BASE page phys: half phys % 2 of TARGET block phys // 2
+            K[t:t + n] = base_values(base_page(k_target, phys)[:n])
+            V[t:t + n] = base_values(base_page(v_target, phys)[:n])
         else:
             raise ValueError(f"fidelity flag {flag} is neither TARGET nor COMPACT")
     return K, V

@@ -41,11 +41,13 @@ def parse():
     ap.add_argument("--no-flags", action="store_true", help="single-pool path (no per-page flag reads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time")
-    ap.add_argument("--workload", choices=("decode", "prefill", "mixed", "writer"), default="decode",
+    ap.add_argument("--workload", choices=("decode", "prefill", "mixed", "writer", "elastic"),
+                    default="decode",
                     help="decode: the headline line; prefill: 32 x 8192 compact-prefill route "
                          "(gather + causal prefill, 4 chunks); mixed: the 36-layer mixed batch; "
                          "writer: cache writer (page quantizer over the 32 x 8192 prompt rows, "
-                         "TARGET append)")
+                         "TARGET append); elastic: ElasticKV BASE decode (structured and general "
+                         "paths) and the demotion pack")
     ap.add_argument("--layers", type=int, default=36, help="mixed workload: layers per step")
     ap.add_argument("--distinct-layers", type=int, default=4,
                     help="mixed workload: distinct generated layers cycled over the step")
@@ -79,6 +81,9 @@ def main():
         return
     if args.workload == "writer":
         bench_writer(args)
+        return
+    if args.workload == "elastic":
+        bench_elastic(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the decode hot path on a single MI355X "
@@ -444,6 +449,88 @@ def bench_writer(args):
                    "frac": round((ar + aw) / ta / 1e9 / HBM_PEAK_GBPS, 4),
                    "decode_step_32_tokens_us": round(td * 1e6, 2)},
         "cpu_baseline": cpu,
+        "input_generation_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_elastic(args):
+    """ElasticKV BASE decode, B 32 x context 8192 (sink pair and 512 recent tokens TARGET,
+    the middle 478 pages BASE): the structured path (per-sequence bounds), the general path
+    (per-page flags), all-TARGET decode of the same batch for reference, and the pack."""
+    import torch
+
+    from mixed_precision_paged_amd import bytemodel, ekv, synth
+
+    t0 = time.time()
+    e = synth.elastic_decode_case(seed=6)
+    gen_s = time.time() - t0
+    c = e.paged
+    B, Hq, Hkv, D = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    kv = ekv.paged_kv(Hkv, D, dev(c.k_target), dev(c.v_target))
+    q, pt, fl, lens, bounds = dev(c.q), dev(c.page_table), dev(c.fidelity), dev(c.seq_lens), dev(e.base_bounds)
+    out = torch.empty((B, Hq, D), dtype=torch.float16, device="cuda")
+    pps = ekv.ekv_decode_plan_pages_per_split(c.seq_lens, Hkv)
+    scratch = torch.empty(ekv.ekv_decode_scratch_bytes(B, Hq, Hkv, D, c.max_seq_len, pps), dtype=torch.uint8,
+                          device="cuda")
+    stream = torch.cuda.current_stream()
+    # the same batch with every page TARGET (fresh pools, so no cache reuse across runs)
+    t = synth.make_paged_case(6, [8192] * B, Hq, Hkv, D, compact_frac=0.0)
+    kv_t = ekv.paged_kv(Hkv, D, dev(t.k_target), dev(t.v_target))
+    pt_t, lens_t = dev(t.page_table), dev(t.seq_lens)
+
+    def timed(fn, steps):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        evs = _events(steps)
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+    steps = max(1, min(args.steps, 50))
+    ts = timed(lambda: ekv.ekv_decode_attention_elastic(kv, q, pt, None, bounds, True, lens, c.max_seq_len,
+                                                        c.sm_scale, out, None, scratch, pps, stream), steps)
+    tg = timed(lambda: ekv.ekv_decode_attention_elastic(kv, q, pt, fl, None, True, lens, c.max_seq_len,
+                                                        c.sm_scale, out, None, scratch, pps, stream), steps)
+    tt = timed(lambda: ekv.ekv_decode_attention(kv_t, q, pt_t, None, lens_t, 8192, c.sm_scale, out, None,
+                                                scratch, pps, stream), steps)
+    b_s = bytemodel.decode_bytes(c.seq_lens, c.fidelity, Hq, Hkv, D, flags_read=False, bounds_read=True)
+    b_g = bytemodel.decode_bytes(c.seq_lens, c.fidelity, Hq, Hkv, D, flags_read=True)
+    b_t = bytemodel.decode_bytes(t.seq_lens, t.fidelity, Hq, Hkv, D, flags_read=False)
+    # demotion pack of 4,096 pairs of a separate TARGET pool
+    n_pairs = 4096
+    torch.manual_seed(7)
+    kp = torch.randn((2 * n_pairs, 16, Hkv, D), device="cuda").half()
+    vp = torch.randn_like(kp)
+    kv_p = ekv.paged_kv(Hkv, D, kp, vp)
+    perm = torch.randperm(2 * n_pairs, device="cuda").int()
+    src_a, src_b = perm[:n_pairs].contiguous(), perm[n_pairs:].contiguous()
+    tp = timed(lambda: ekv.ekv_pack_base_pairs(kv_p, src_a, src_b, src_a, stream), max(1, min(steps, 10)))
+    pr, pw = bytemodel.pack_bytes(n_pairs, Hkv, D)
+    gb = lambda n, sec: round(n / sec / 1e9, 1)
+    line = {
+        "metric": "ElasticKV BASE decode HBM GB/s (structured TARGET-BASE-TARGET path), B=32 ctx 8K",
+        "value": gb(b_s, ts), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(ts * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "elastic decode: batch 32, context 8192, 32 q / 8 KV heads, head dim 128; "
+                               "pages 0-1 and the last 32 TARGET, pages 2-479 BASE (high FP16 byte, two "
+                               "pages per TARGET block) (seed 6)", "pages_per_split": pps},
+        "roofline": {"bound": "hbm", "kernel": "ekv_decode_attention_elastic (structured)",
+                     "achieved": gb(b_s, ts), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(b_s / ts / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_call_us": round(ts * 1e6, 2), "algorithmic_bytes": b_s},
+        "tokens_per_s": round(B / ts, 1),
+        "general_path": {"avg_call_us": round(tg * 1e6, 2), "gbps": gb(b_g, tg), "algorithmic_bytes": b_g},
+        "all_target_same_batch": {"avg_call_us": round(tt * 1e6, 2), "gbps": gb(b_t, tt),
+                                  "algorithmic_bytes": b_t, "speedup_of_structured_base": round(tt / ts, 3)},
+        "pack": {"pairs": n_pairs, "avg_call_us": round(tp * 1e6, 2), "gbps": gb(pr + pw, tp),
+                 "frac": round((pr + pw) / tp / 1e9 / HBM_PEAK_GBPS, 4)},
         "input_generation_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)

@@ -50,6 +50,8 @@ extern "C" {
 #define EKV_PAGE_SIZE 16
 #define EKV_FIDELITY_TARGET 0   /* FP16 K + FP16 V                        */
 #define EKV_FIDELITY_COMPACT 1  /* FP16 K + E4M3 V + fp32 scale/page/head  */
+#define EKV_FIDELITY_BASE 2     /* ElasticKV BASE: high FP16 byte of K and V,
+                                   two pages per TARGET block (elastic decode) */
 #define EKV_MAX_PREFILL_TOKENS 8192 /* [asym] route rule: prompts of at most 8,192 tokens */
 
 typedef enum {
@@ -76,7 +78,12 @@ typedef enum { EKV_F16 = 0, EKV_F32 = 1 } ekv_dtype;
  *   v_scale            : fp32 [n_compact_pages][num_kv_heads]; the value of a
  *                        compact element is e4m3(byte) * v_scale[page][head]
  * A pool that is not used may be NULL with its page count 0.  Page counts
- * must be below 2^30.  Scales must be positive normal fp32 values.
+ * must be below 2^28.  Scales must be positive normal fp32 values.
+ *
+ * ElasticKV BASE pages ([ekv] section 3.1, figure 3(b)) live in the TARGET
+ * pools: BASE page id b is half (b & 1) of TARGET block b >> 1, i.e. the
+ * block's first or second 16 x num_kv_heads x head_dim bytes, laid out
+ * [slot][kv_head][d]; each byte is the high byte of an FP16 value.
  */
 typedef struct {
   const void* k_target;
@@ -162,6 +169,32 @@ ekv_status ekv_decode_attention(const ekv_paged_kv* kv, const void* q, int32_t b
                                 int32_t max_seq_len, float sm_scale, void* out, ekv_dtype out_dtype,
                                 float* lse, int32_t pages_per_split, void* scratch,
                                 size_t scratch_bytes, void* stream);
+
+/*
+ * Elastic decode: ekv_decode_attention over pages that may also be ElasticKV
+ * BASE pages.  [ekv] section 3.2 and appendix B.3: a batch-level BASE
+ * indicator lets batches without BASE skip the elastic machinery; batches
+ * with BASE carry either a per-page mode table (general path) or per-sequence
+ * boundaries of the common TARGET-BASE-TARGET layout (structured path); a
+ * BASE value is its stored byte in the high position with a zero low byte,
+ * read in registers, with no scale.
+ *
+ *   has_base     0: exactly ekv_decode_attention (flags 0/1; base_bounds NULL).
+ *                1: the batch may hold BASE pages; then give exactly one of
+ *   fidelity     u8 [batch][pt_stride] with values 0, 1 or 2 (EKV_FIDELITY_*),
+ *   base_bounds  int32 [batch][2] (device): logical pages [lo, hi) of
+ *                sequence b are BASE, all others TARGET (no flag table).
+ * Other arguments, scratch sizing and the NaN rule for bad ids or flags are
+ * those of ekv_decode_attention.  has_base = 1 needs a non-empty TARGET pool.
+ */
+ekv_status ekv_decode_attention_elastic(const ekv_paged_kv* kv, const void* q, int32_t batch,
+                                        int32_t num_q_heads, const int32_t* page_table,
+                                        int32_t pt_stride, const uint8_t* fidelity,
+                                        const int32_t* base_bounds, int32_t has_base,
+                                        const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                        void* out, ekv_dtype out_dtype, float* lse,
+                                        int32_t pages_per_split, void* scratch, size_t scratch_bytes,
+                                        void* stream);
 
 /*
  * Compact-prefill gather: copy the listed compact pages into a bounded FP16
@@ -292,6 +325,26 @@ ekv_status ekv_quantize_pages(const ekv_paged_kv* kv, const void* k_src, const v
                               int64_t src_rows, const int32_t* src_row_start,
                               const int32_t* n_valid, const int32_t* dst_pages, int32_t n_pages,
                               void* stream);
+
+/*
+ * ElasticKV demotion pack: TARGET pairs -> BASE blocks.  [ekv] section 3.1
+ * and appendix B.2: the GPU packs the high-order bytes of a pair's two TARGET
+ * blocks into one block (the pair's BASE layout) and the other block is
+ * returned to the allocator.
+ *
+ *   kv            WRITES through kv->k_target and kv->v_target.
+ *   src_a, src_b  int32 [n_pairs] (device): the pair's TARGET blocks.
+ *   dst           int32 [n_pairs] (device): the block that receives the pair;
+ *                 half 0 = high bytes of src_a (BASE page 2 dst), half 1 =
+ *                 high bytes of src_b (BASE page 2 dst + 1), for K and V.
+ *                 dst may equal src_a or src_b (in place: both blocks are
+ *                 read before it is written).  Blocks of different pairs
+ *                 must not overlap.
+ * A pair with an id outside the TARGET pool is skipped.  num_kv_heads *
+ * head_dim above 2048 returns EKV_ERR_UNSUPPORTED.
+ */
+ekv_status ekv_pack_base_pairs(const ekv_paged_kv* kv, const int32_t* src_a, const int32_t* src_b,
+                               const int32_t* dst, int32_t n_pairs, void* stream);
 
 /*
  * Diagnostic for the device E4M3 decoding used by the kernels: converts n

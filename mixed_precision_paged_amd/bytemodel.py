@@ -38,13 +38,16 @@ def token_slots(pool_bytes: int, layers: int, kv_heads: int, head_dim: int, layo
 
 
 def decode_bytes(seq_lens, fidelity, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                 out_bytes: int = 2, lse: bool = False, flags_read: bool = True) -> int:
+                 out_bytes: int = 2, lse: bool = False, flags_read: bool = True,
+                 bounds_read: bool = False) -> int:
     """Bytes one decode launch must move.
 
-    K: 2 B per element for every valid token; V: 2 B (TARGET) or 1 B
-    (COMPACT) per element; one fp32 scale per compact page per KV head; one
-    int32 page id (and one uint8 flag when flags are read) per page; the FP16
-    query; the output (and fp32 LSE when requested).
+    K: 2 B per element for every valid token (1 B on an ElasticKV BASE page);
+    V: 2 B (TARGET) or 1 B (COMPACT, BASE) per element; one fp32 scale per
+    compact page per KV head; one int32 page id (and one uint8 flag when flags
+    are read) per page; two int32 BASE bounds per sequence when the structured
+    layout is read instead of flags; the FP16 query; the output (and fp32 LSE
+    when requested).
     """
     lens = np.asarray(seq_lens, dtype=np.int64)
     fid = np.asarray(fidelity)
@@ -54,16 +57,25 @@ def decode_bytes(seq_lens, fidelity, num_q_heads: int, num_kv_heads: int, head_d
         pages = int((n + PAGE - 1) // PAGE)
         toks = np.minimum(PAGE, n - PAGE * np.arange(pages))
         kinds = fid[b, :pages].astype(np.int64)
-        total += int(toks.sum()) * HD * 2                         # K16
-        total += int((toks * np.where(kinds == 1, 1, 2)).sum()) * HD   # V16 or V8
+        total += int((toks * np.where(kinds == 2, 1, 2)).sum()) * HD   # K16 or BASE K
+        total += int((toks * np.where(kinds == 0, 2, 1)).sum()) * HD   # V16, V8 or BASE V
         total += int((kinds == 1).sum()) * num_kv_heads * 4        # scales
         total += pages * 4 + (pages if flags_read else 0)          # page ids, flags
     B = lens.shape[0]
+    if bounds_read:
+        total += B * 8                                             # BASE bounds
     total += B * num_q_heads * head_dim * 2                        # q
     total += B * num_q_heads * head_dim * out_bytes                # out
     if lse:
         total += B * num_q_heads * 4
     return total
+
+
+def pack_bytes(n_pairs: int, num_kv_heads: int, head_dim: int):
+    """(read, written) bytes of one ElasticKV pack launch: per pair two fp16 TARGET
+    blocks of K and of V are read and one block of each is written, plus 3 int32 ids."""
+    block = PAGE * num_kv_heads * head_dim * 2
+    return n_pairs * (4 * block + 12), n_pairs * 2 * block
 
 
 def gather_bytes(n_pages: int, num_kv_heads: int, head_dim: int):

@@ -69,16 +69,28 @@ struct Slot {
 // `kqoff` (token l%16, 16 B chunk l/16) and `voff` (token 4(l/16), d chunk
 // l%16) are per-lane byte offsets; the token step of V goes in the scalar
 // offset.  Each V load instruction covers 4 whole token rows.
-template <int D>
+// BASE pages (ElasticKV high bytes; only in the HAS_BASE variants) hold one
+// byte per K element: a lane's 8 K values of a k-step are 8 bytes at `kqoff8`,
+// loaded into the low half of r.k[kb] and expanded before the MFMA; their V
+// bytes take the compact path's byte layout.
+template <int D, bool HAS_BASE>
 __device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* kbase,
                                           const char* vbase, uint32_t kbytes, uint32_t vbytes,
-                                          uint32_t kqoff, uint32_t voff16, uint32_t voff8,
+                                          uint32_t kqoff, uint32_t kqoff8, uint32_t voff16, uint32_t voff8,
                                           uint32_t krow, uint32_t vrow) {
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, kbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, vbytes, kBufferFlags);
+  if (HAS_BASE && kind == 2) {
 #pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb)
-    r.k[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, kqoff + 64u * kb, 0, 0));
+    for (int kb = 0; kb < D / 32; ++kb) {
+      const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(kr, kqoff8 + 32u * kb, 0, 0);
+      r.k[kb] = __builtin_bit_cast(f16x8, u32x4{a.x, a.y, 0u, 0u});
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb)
+      r.k[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, kqoff + 64u * kb, 0, 0));
+  }
   if (kind == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -115,14 +127,22 @@ __device__ __forceinline__ f16x4 pack4(float a, float b, float c, float d) {
   return f16x4{(f16)a, (f16)b, (f16)c, (f16)d};
 }
 
-template <int D, int G>
+// Eight BASE bytes (two words) -> eight fp16 values: each byte in the high
+// position of its 16 bits, the low byte zero (selector 0x0C gives 0x00).
+__device__ __forceinline__ f16x8 base_expand(f16x8 raw) {
+  const u32x4 w = __builtin_bit_cast(u32x4, raw);
+  return __builtin_bit_cast(f16x8, u32x4{perm(w.x, w.x, 0x010C000Cu), perm(w.x, w.x, 0x030C020Cu),
+                                         perm(w.y, w.y, 0x010C000Cu), perm(w.y, w.y, 0x030C020Cu)});
+}
+
+template <int D, int G, bool HAS_BASE>
 __device__ __forceinline__ void process_page(State<D, G>& st, PageRegs<D>& r, const DecodeParams& p,
                                              int kind, float scale, int pg, int len, int lane) {
   constexpr int NE = D / 16;  // PV MFMAs (d columns per lane)
   const int tq = lane >> 4;
   // Compact scale s = 2^e * f, f in [1, 2): the conversion applies the exact power of two,
   // p carries f.  (Scales are positive normal fp32 values.)
-  const uint32_t sbits = kind ? __builtin_bit_cast(uint32_t, scale) : 0x3F800000u;
+  const uint32_t sbits = kind == 1 ? __builtin_bit_cast(uint32_t, scale) : 0x3F800000u;
   const float s_pow2 = as_f32(sbits & 0x7F800000u);
   const float s_frac = as_f32((sbits & 0x807FFFFFu) | 0x3F800000u);
   const bool partial = pg * kPage + kPage > len;  // wavefront-uniform
@@ -130,9 +150,15 @@ __device__ __forceinline__ void process_page(State<D, G>& st, PageRegs<D>& r, co
   // S^T = K . Q^T on the matrix cores: lane l gets the scores of head l%16 for
   // tokens 4(l/16)+i of the page (i < 4).
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (HAS_BASE && kind == 2) {
 #pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb)
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(r.k[kb], st.qb[kb], sacc, 0, 0, 0);
+    for (int kb = 0; kb < D / 32; ++kb)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(base_expand(r.k[kb]), st.qb[kb], sacc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(r.k[kb], st.qb[kb], sacc, 0, 0, 0);
+  }
   float x[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = sacc[i] * p.scale_log2;
@@ -185,6 +211,18 @@ __device__ __forceinline__ void process_page(State<D, G>& st, PageRegs<D>& r, co
       vb[2 * w] = __builtin_bit_cast(f16x4, u32x2{e0, e1});
       vb[2 * w + 1] = __builtin_bit_cast(f16x4, u32x2{o0, o1});
     }
+  } else if (HAS_BASE && kind == 2) {
+    // BASE bytes: column c of dword w is d = 4w + c; each token's byte goes to
+    // the high position of its fp16 (tokens 0, 1 from rows 0, 1; 2, 3 from 2, 3)
+#pragma unroll
+    for (int w = 0; w < NE / 4; ++w) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t sel = 0x040C000Cu + 0x01000100u * c;
+        vb[4 * w + c] = __builtin_bit_cast(f16x4, u32x2{perm(r.v[1][w], r.v[0][w], sel),
+                                                        perm(r.v[3][w], r.v[2][w], sel)});
+      }
+    }
   } else {
 #pragma unroll
     for (int w = 0; w < NE / 4; ++w) {
@@ -203,8 +241,16 @@ __device__ __forceinline__ void process_page(State<D, G>& st, PageRegs<D>& r, co
   }
 }
 
-template <int D, int G, bool FLAGS>
+// MODE 0: every page has kind p.uniform_kind (no flag table); 1: per-page flags
+// TARGET/COMPACT; 2: per-page flags that may also be BASE (the batch-level
+// BASE indicator is set); 3: structured TARGET-BASE-TARGET layout: logical
+// pages [base_bounds[b][0], base_bounds[b][1]) of sequence b are BASE, all
+// others TARGET, with no flag table.
+template <int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads, kMinWaves) void decode_splitk_kernel(DecodeParams p) {
+  constexpr bool FLAGS = MODE == 1 || MODE == 2;
+  constexpr bool HAS_BASE = MODE >= 2;
+  constexpr int KBITS = HAS_BASE ? 2 : 1;  // kind bits in the staged page metadata
   constexpr int NE = D / 16;
   __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
@@ -237,18 +283,23 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void decode_splitk_kernel(Deco
 #pragma unroll
   for (int e = 0; e < NE; ++e) st.acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Stage this split's page metadata in LDS once: (phys << 1 | kind), or -1
-  // for an out-of-range id or unknown flag.  Per-page reads are then LDS
+  // Stage this split's page metadata in LDS once: (phys << KBITS | kind), or
+  // -1 for an out-of-range id or unknown flag.  Per-page reads are then LDS
   // reads, which never wait on the vector-memory counter of in-flight pages.
+  // A BASE page id names half (id & 1) of TARGET block id >> 1.
   {
     const int32_t* pt = p.page_table + (int64_t)b * p.pt_stride;
     const uint8_t* fl = FLAGS ? p.fidelity + (int64_t)b * p.pt_stride : nullptr;
+    const int blo = MODE == 3 ? p.base_bounds[2 * b] : 0;
+    const int bhi = MODE == 3 ? p.base_bounds[2 * b + 1] : 0;
     for (int i = threadIdx.x; i < pend - pbeg; i += kThreads) {
       const int phys = pt[pbeg + i];
-      const int kind = FLAGS ? (int)fl[pbeg + i] : p.uniform_kind;
+      const int j = pbeg + i;
+      const int kind = FLAGS ? (int)fl[j] : MODE == 3 ? (j >= blo && j < bhi ? 2 : 0) : p.uniform_kind;
       const bool ok = (kind == 0 && (unsigned)phys < (unsigned)p.n_target) ||
-                      (kind == 1 && (unsigned)phys < (unsigned)p.n_compact);
-      s_meta[i] = ok ? (phys << 1) | kind : -1;
+                      (kind == 1 && (unsigned)phys < (unsigned)p.n_compact) ||
+                      (HAS_BASE && kind == 2 && (unsigned)phys < 2u * (unsigned)p.n_target);
+      s_meta[i] = ok ? (phys << KBITS) | kind : -1;
     }
   }
   __syncthreads();
@@ -257,6 +308,7 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void decode_splitk_kernel(Deco
   const uint32_t krow = (uint32_t)p.num_kv_heads * D * 2u;   // bytes per token row, fp16
   const uint32_t vrow = (uint32_t)p.num_kv_heads * D;        // bytes per token row, E4M3
   const uint32_t kqoff = (uint32_t)(lane & 15) * krow + 16u * (lane >> 4);      // K: token l%16
+  const uint32_t kqoff8 = (uint32_t)(lane & 15) * vrow + 8u * (lane >> 4);      // BASE K bytes
   const uint32_t voff16 = 4u * (lane >> 4) * krow + (uint32_t)(lane & 15) * (D / 8);  // V16: tokens 4(l/16)+i
   const uint32_t voff8 = 4u * (lane >> 4) * vrow + (uint32_t)(lane & 15) * (D / 16);  // V8
   const int64_t kpage = (int64_t)kPage * krow, vpage8 = (int64_t)kPage * vrow;
@@ -267,17 +319,26 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void decode_splitk_kernel(Deco
     if (pq >= pend) return;
     const int m = __builtin_amdgcn_readfirstlane(s_meta[pq - pbeg]);
     if (m < 0) { bad = true; return; }
-    const int phys = m >> 1;
-    sl.kind = m & 1;
+    const int phys = m >> KBITS;
+    sl.kind = m & ((1 << KBITS) - 1);
     sl.ok = true;
-    const char* kb = reinterpret_cast<const char*>(sl.kind ? p.k_compact : p.k_target) +
-                     phys * kpage + (int64_t)g * D * 2;
-    const char* vb = sl.kind ? reinterpret_cast<const char*>(p.v_compact) + phys * vpage8 + (int64_t)g * D
-                             : reinterpret_cast<const char*>(p.v_target) + phys * kpage + (int64_t)g * D * 2;
-    const uint32_t kbytes = (uint32_t)kpage - (uint32_t)g * D * 2;
-    const uint32_t vbytes = sl.kind ? (uint32_t)vpage8 - (uint32_t)g * D : kbytes;
-    sl.scale = sl.kind ? p.v_scale[(int64_t)phys * p.num_kv_heads + g] : 1.0f;
-    load_page<D>(sl.r, sl.kind, kb, vb, kbytes, vbytes, kqoff, voff16, voff8, krow, vrow);
+    const char* kb;
+    const char* vb;
+    uint32_t kbytes, vbytes;
+    if (HAS_BASE && sl.kind == 2) {  // half (phys & 1) of TARGET block phys >> 1, bytes
+      const int64_t off = (int64_t)(phys >> 1) * kpage + (int64_t)(phys & 1) * vpage8 + (int64_t)g * D;
+      kb = reinterpret_cast<const char*>(p.k_target) + off;
+      vb = reinterpret_cast<const char*>(p.v_target) + off;
+      kbytes = vbytes = (uint32_t)vpage8 - (uint32_t)g * D;
+    } else {
+      kb = reinterpret_cast<const char*>(sl.kind ? p.k_compact : p.k_target) + phys * kpage + (int64_t)g * D * 2;
+      vb = sl.kind ? reinterpret_cast<const char*>(p.v_compact) + phys * vpage8 + (int64_t)g * D
+                   : reinterpret_cast<const char*>(p.v_target) + phys * kpage + (int64_t)g * D * 2;
+      kbytes = (uint32_t)kpage - (uint32_t)g * D * 2;
+      vbytes = sl.kind ? (uint32_t)vpage8 - (uint32_t)g * D : kbytes;
+    }
+    sl.scale = sl.kind == 1 ? p.v_scale[(int64_t)phys * p.num_kv_heads + g] : 1.0f;
+    load_page<D, HAS_BASE>(sl.r, sl.kind, kb, vb, kbytes, vbytes, kqoff, kqoff8, voff16, voff8, krow, vrow);
   };
   // kSlots register page buffers: pages pg+4 .. pg+4(kSlots-1) load while page pg
   // computes.  Slots are named variables (never an indexed array) so they stay
@@ -287,7 +348,7 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void decode_splitk_kernel(Deco
   Slot<D> s0, s1, s2, s3, s4, s5;
 #define EKV_STEP(CUR, NXT)                                                        \
   issue(NXT, pg + (kSlots - 1) * kWaves);                                         \
-  if (CUR.ok) process_page<D, G>(st, CUR.r, p, CUR.kind, CUR.scale, pg, len, lane); \
+  if (CUR.ok) process_page<D, G, HAS_BASE>(st, CUR.r, p, CUR.kind, CUR.scale, pg, len, lane); \
   pg += kWaves;                                                                   \
   if (pg >= pend) break;
   issue(s0, pg);
@@ -425,10 +486,13 @@ hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid = kHeadMajorGrid ? dim3(p.num_kv_heads, p.n_splits, p.batch)
                                    : dim3(p.n_splits, p.num_kv_heads, p.batch);
   if (p.n_splits > 0) {
-    if (p.fidelity)
-      hipLaunchKernelGGL((decode_splitk_kernel<D, G, true>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_splitk_kernel<D, G, false>), grid, dim3(kThreads), 0, stream, p);
+    const int mode = p.has_base ? (p.fidelity ? 2 : 3) : (p.fidelity ? 1 : 0);
+    switch (mode) {
+      case 0: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 0>), grid, dim3(kThreads), 0, stream, p); break;
+      case 1: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 1>), grid, dim3(kThreads), 0, stream, p); break;
+      case 2: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 2>), grid, dim3(kThreads), 0, stream, p); break;
+      default: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 3>), grid, dim3(kThreads), 0, stream, p); break;
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -51,8 +51,8 @@ ekv_status check_kv(const ekv_paged_kv* kv, bool need_target, bool need_compact)
   if (!kv) return fail(EKV_ERR_INVALID_ARG, "kv descriptor is NULL");
   if (kv->page_size != EKV_PAGE_SIZE) return fail(EKV_ERR_INVALID_ARG, "page_size %d != %d", kv->page_size, EKV_PAGE_SIZE);
   if (kv->n_target_pages < 0 || kv->n_compact_pages < 0) return fail(EKV_ERR_INVALID_ARG, "negative pool size");
-  if (kv->n_target_pages >= (1 << 30) || kv->n_compact_pages >= (1 << 30))
-    return fail(EKV_ERR_UNSUPPORTED, "pools of 2^30 pages or more are not supported");
+  if (kv->n_target_pages >= (1 << 28) || kv->n_compact_pages >= (1 << 28))
+    return fail(EKV_ERR_UNSUPPORTED, "pools of 2^28 pages or more are not supported");
   if (need_target || kv->n_target_pages > 0) {
     if (!kv->k_target || !kv->v_target) return fail(EKV_ERR_INVALID_ARG, "target pool pointer is NULL");
     if (!aligned16(kv->k_target) || !aligned16(kv->v_target)) return fail(EKV_ERR_INVALID_ARG, "target pool not 16-byte aligned");
@@ -118,12 +118,15 @@ size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_
   return ekv::decode_scratch_bytes(batch, num_q_heads, num_kv_heads, head_dim, splits);
 }
 
-ekv_status ekv_decode_attention(const ekv_paged_kv* kv, const void* q, int32_t batch,
-                                int32_t num_q_heads, const int32_t* page_table, int32_t pt_stride,
-                                const uint8_t* fidelity, const int32_t* seq_lens,
-                                int32_t max_seq_len, float sm_scale, void* out, ekv_dtype out_dtype,
-                                float* lse, int32_t pages_per_split, void* scratch,
-                                size_t scratch_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+ekv_status decode_impl(const ekv_paged_kv* kv, const void* q, int32_t batch, int32_t num_q_heads,
+                       const int32_t* page_table, int32_t pt_stride, const uint8_t* fidelity,
+                       const int32_t* base_bounds, int32_t has_base, const int32_t* seq_lens,
+                       int32_t max_seq_len, float sm_scale, void* out, ekv_dtype out_dtype, float* lse,
+                       int32_t pages_per_split, void* scratch, size_t scratch_bytes, void* stream) {
   if (!kv) return fail(EKV_ERR_INVALID_ARG, "kv descriptor is NULL");
   ekv_status s = check_geometry(num_q_heads, kv->num_kv_heads, kv->head_dim);
   if (s != EKV_OK) return s;
@@ -140,7 +143,13 @@ ekv_status ekv_decode_attention(const ekv_paged_kv* kv, const void* q, int32_t b
   if (pt_stride < max_pages || pt_stride <= 0) return fail(EKV_ERR_INVALID_ARG, "pt_stride %d < ceil(max_seq_len/16) = %d", pt_stride, max_pages);
   const bool has_t = kv->n_target_pages > 0, has_c = kv->n_compact_pages > 0;
   int32_t uniform_kind = 0;
-  if (!fidelity) {
+  if (has_base != 0 && has_base != 1) return fail(EKV_ERR_INVALID_ARG, "has_base must be 0 or 1");
+  if (!has_base && base_bounds) return fail(EKV_ERR_INVALID_ARG, "base_bounds needs has_base = 1");
+  if (has_base) {
+    if (!has_t) return fail(EKV_ERR_INVALID_ARG, "BASE pages live in the TARGET pool, which is empty");
+    if (!fidelity && !base_bounds) return fail(EKV_ERR_INVALID_ARG, "has_base needs fidelity flags or base_bounds");
+    if (fidelity && base_bounds) return fail(EKV_ERR_INVALID_ARG, "give fidelity flags or base_bounds, not both");
+  } else if (!fidelity) {
     if (has_t == has_c) return fail(EKV_ERR_INVALID_ARG, "fidelity may be NULL only when exactly one pool is non-empty");
     uniform_kind = has_c ? EKV_FIDELITY_COMPACT : EKV_FIDELITY_TARGET;
   }
@@ -170,6 +179,8 @@ ekv_status ekv_decode_attention(const ekv_paged_kv* kv, const void* q, int32_t b
   p.pt_stride = pt_stride;
   p.fidelity = fidelity;
   p.uniform_kind = uniform_kind;
+  p.has_base = has_base;
+  p.base_bounds = base_bounds;
   p.seq_lens = seq_lens;
   p.batch = batch;
   p.num_q_heads = num_q_heads;
@@ -188,6 +199,34 @@ ekv_status ekv_decode_attention(const ekv_paged_kv* kv, const void* q, int32_t b
   p.out_f32 = out_dtype == EKV_F32;
   p.lse = lse;
   return hip_status(ekv::launch_decode(p, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+ekv_status ekv_decode_attention(const ekv_paged_kv* kv, const void* q, int32_t batch,
+                                int32_t num_q_heads, const int32_t* page_table, int32_t pt_stride,
+                                const uint8_t* fidelity, const int32_t* seq_lens,
+                                int32_t max_seq_len, float sm_scale, void* out, ekv_dtype out_dtype,
+                                float* lse, int32_t pages_per_split, void* scratch,
+                                size_t scratch_bytes, void* stream) {
+  return decode_impl(kv, q, batch, num_q_heads, page_table, pt_stride, fidelity, nullptr, 0, seq_lens,
+                     max_seq_len, sm_scale, out, out_dtype, lse, pages_per_split, scratch, scratch_bytes,
+                     stream);
+}
+
+ekv_status ekv_decode_attention_elastic(const ekv_paged_kv* kv, const void* q, int32_t batch,
+                                        int32_t num_q_heads, const int32_t* page_table,
+                                        int32_t pt_stride, const uint8_t* fidelity,
+                                        const int32_t* base_bounds, int32_t has_base,
+                                        const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                        void* out, ekv_dtype out_dtype, float* lse,
+                                        int32_t pages_per_split, void* scratch, size_t scratch_bytes,
+                                        void* stream) {
+  return decode_impl(kv, q, batch, num_q_heads, page_table, pt_stride, fidelity, base_bounds, has_base,
+                     seq_lens, max_seq_len, sm_scale, out, out_dtype, lse, pages_per_split, scratch,
+                     scratch_bytes, stream);
 }
 
 ekv_status ekv_gather_compact_pages(const ekv_paged_kv* kv, const int32_t* page_ids,
@@ -378,6 +417,32 @@ ekv_status ekv_quantize_pages(const ekv_paged_kv* kv, const void* k_src, const v
   p.num_kv_heads = kv->num_kv_heads;
   p.head_dim = kv->head_dim;
   return hip_status(ekv::launch_quantize(p, static_cast<hipStream_t>(stream)), "quantize launch");
+}
+
+ekv_status ekv_pack_base_pairs(const ekv_paged_kv* kv, const int32_t* src_a, const int32_t* src_b,
+                               const int32_t* dst, int32_t n_pairs, void* stream) {
+  if (!kv) return fail(EKV_ERR_INVALID_ARG, "kv descriptor is NULL");
+  if (kv->head_dim != 64 && kv->head_dim != 128) return fail(EKV_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", kv->head_dim);
+  if (kv->num_kv_heads <= 0) return fail(EKV_ERR_INVALID_ARG, "num_kv_heads must be positive");
+  if ((int64_t)kv->num_kv_heads * kv->head_dim > 2048)
+    return fail(EKV_ERR_UNSUPPORTED, "num_kv_heads * head_dim = %d exceeds 2048", kv->num_kv_heads * kv->head_dim);
+  ekv_status s = check_kv(kv, true, false);
+  if (s != EKV_OK) return s;
+  if (n_pairs < 0) return fail(EKV_ERR_INVALID_ARG, "n_pairs %d < 0", n_pairs);
+  if (n_pairs == 0) return ok();
+  if (n_pairs > 0x7FFFFFFF / 2) return fail(EKV_ERR_UNSUPPORTED, "too many pairs");
+  if (!src_a || !src_b || !dst) return fail(EKV_ERR_INVALID_ARG, "src_a, src_b and dst are required");
+  ekv::PackParams p{};
+  p.k_target = static_cast<uint16_t*>(const_cast<void*>(kv->k_target));
+  p.v_target = static_cast<uint16_t*>(const_cast<void*>(kv->v_target));
+  p.n_target = kv->n_target_pages;
+  p.src_a = src_a;
+  p.src_b = src_b;
+  p.dst = dst;
+  p.n_pairs = n_pairs;
+  p.num_kv_heads = kv->num_kv_heads;
+  p.head_dim = kv->head_dim;
+  return hip_status(ekv::launch_pack_base(p, static_cast<hipStream_t>(stream)), "pack launch");
 }
 
 ekv_status ekv_e4m3_to_f16(const uint8_t* codes, int32_t n, void* out, int32_t method, void* stream) {

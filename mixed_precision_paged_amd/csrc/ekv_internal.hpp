@@ -18,8 +18,10 @@ struct DecodeParams {
   const uint16_t* q;
   const int32_t* page_table;
   int32_t pt_stride;
-  const uint8_t* fidelity;  // NULL: every page has kind `uniform_kind`
+  const uint8_t* fidelity;  // NULL: every page has kind `uniform_kind` (or base_bounds)
   int32_t uniform_kind;
+  int32_t has_base;              // batch-level ElasticKV BASE indicator
+  const int32_t* base_bounds;    // [batch][2] structured BASE range, when has_base and no flags
   const int32_t* seq_lens;
   int32_t batch, num_q_heads, num_kv_heads, head_dim, max_seq_len;
   int32_t pages_per_split, n_splits;
@@ -100,6 +102,17 @@ struct QuantizeParams {
   int32_t num_kv_heads, head_dim;
 };
 
+struct PackParams {
+  uint16_t* k_target;
+  uint16_t* v_target;
+  int32_t n_target;
+  const int32_t* src_a;  // [n_pairs]
+  const int32_t* src_b;
+  const int32_t* dst;
+  int32_t n_pairs;
+  int32_t num_kv_heads, head_dim;
+};
+
 // Split plan shared by the scratch query and the launch.
 int32_t decode_auto_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages);
 size_t decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -110,6 +123,7 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
+hipError_t launch_pack_base(const PackParams& p, hipStream_t stream);
 hipError_t launch_e4m3_to_f16(const uint8_t* codes, int32_t n, uint16_t* out, int32_t method,
                               hipStream_t stream);
 

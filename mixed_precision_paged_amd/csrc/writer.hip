@@ -175,7 +175,57 @@ __global__ __launch_bounds__(kWriterThreads) void quantize_kernel(QuantizeParams
   if (lane == 0) p.v_scale[(int64_t)dst * p.num_kv_heads + h] = s;
 }
 
+// ---------------------------------------------------------------------------
+// ElasticKV demotion pack: pair i's TARGET blocks src_a[i], src_b[i] -> block
+// dst[i] holding their high bytes (half 0 = a, half 1 = b), i.e. BASE pages
+// 2 dst and 2 dst + 1.  One workgroup per (pair, pool): every thread reads its
+// 16-byte chunks of both blocks and keeps their high bytes; a barrier; then
+// the writes, so dst may be a or b (in place).  blockIdx.y: 0 = K pool, 1 = V.
+constexpr int kPackMaxChunks = 8;  // 16-byte chunks of one block per thread (Hkv*D <= 2048)
+
+__global__ __launch_bounds__(kWriterThreads) void pack_base_kernel(PackParams p) {
+  const int pair = blockIdx.x;
+  char* pool = reinterpret_cast<char*>(blockIdx.y == 0 ? p.k_target : p.v_target);
+  const int a = p.src_a[pair], b = p.src_b[pair], d = p.dst[pair];
+  if ((unsigned)a >= (unsigned)p.n_target || (unsigned)b >= (unsigned)p.n_target ||
+      (unsigned)d >= (unsigned)p.n_target)
+    return;  // uniform for the workgroup: nothing is read or written
+  const int chunks = kPage * p.num_kv_heads * p.head_dim / 8;  // per block
+  const int64_t block_bytes = (int64_t)chunks * 16;
+  const uint4* pa = reinterpret_cast<const uint4*>(pool + a * block_bytes);
+  const uint4* pb = reinterpret_cast<const uint4*>(pool + b * block_bytes);
+  uint2 ha[kPackMaxChunks], hb[kPackMaxChunks];
+#pragma unroll
+  for (int j = 0; j < kPackMaxChunks; ++j) {
+    const int c = threadIdx.x + kWriterThreads * j;
+    if (c < chunks) {
+      const uint4 x = pa[c], y = pb[c];
+      // bytes 1, 3, 5, 7 of each 8-byte half: the high bytes of 8 fp16 values
+      ha[j] = make_uint2(perm(x.y, x.x, 0x07050301u), perm(x.w, x.z, 0x07050301u));
+      hb[j] = make_uint2(perm(y.y, y.x, 0x07050301u), perm(y.w, y.z, 0x07050301u));
+    }
+  }
+  __syncthreads();
+  uint2* out0 = reinterpret_cast<uint2*>(pool + d * block_bytes);
+  uint2* out1 = reinterpret_cast<uint2*>(pool + d * block_bytes + block_bytes / 2);
+#pragma unroll
+  for (int j = 0; j < kPackMaxChunks; ++j) {
+    const int c = threadIdx.x + kWriterThreads * j;
+    if (c < chunks) {
+      out0[c] = ha[j];
+      out1[c] = hb[j];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pack_base(const PackParams& p, hipStream_t stream) {
+  if (p.n_pairs == 0) return hipSuccess;
+  if (kPage * p.num_kv_heads * p.head_dim / 8 > kPackMaxChunks * kWriterThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_base_kernel, dim3((unsigned)p.n_pairs, 2), dim3(kWriterThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
   if (p.n_tokens == 0) return hipSuccess;

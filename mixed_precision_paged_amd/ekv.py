@@ -22,6 +22,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PAGE_SIZE = 16
 FIDELITY_TARGET = 0
 FIDELITY_COMPACT = 1
+FIDELITY_BASE = 2
 MAX_PREFILL_TOKENS = 8192
 
 EKV_OK = 0
@@ -35,9 +36,10 @@ EKV_F32 = 1
 
 EXPORTED = (
     "ekv_abi_version", "ekv_status_string", "ekv_last_error", "ekv_decode_pages_per_split",
-    "ekv_decode_plan_pages_per_split",
-    "ekv_decode_scratch_bytes", "ekv_decode_attention", "ekv_gather_compact_pages",
-    "ekv_prefill_attention", "ekv_prefill_paged_attention", "ekv_append_tokens", "ekv_quantize_pages", "ekv_e4m3_to_f16",
+    "ekv_decode_plan_pages_per_split", "ekv_decode_scratch_bytes", "ekv_decode_attention",
+    "ekv_decode_attention_elastic", "ekv_gather_compact_pages", "ekv_prefill_attention",
+    "ekv_prefill_paged_attention", "ekv_append_tokens", "ekv_quantize_pages", "ekv_pack_base_pairs",
+    "ekv_e4m3_to_f16",
 )
 
 
@@ -65,6 +67,12 @@ _lib.ekv_decode_attention.restype = ctypes.c_int
 _lib.ekv_decode_attention.argtypes = [
     ctypes.POINTER(PagedKV), _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _f32, _vp, ctypes.c_int,
     _vp, _i32, _vp, _sz, _vp]
+_lib.ekv_decode_attention_elastic.restype = ctypes.c_int
+_lib.ekv_decode_attention_elastic.argtypes = [
+    ctypes.POINTER(PagedKV), _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _f32, _vp,
+    ctypes.c_int, _vp, _i32, _vp, _sz, _vp]
+_lib.ekv_pack_base_pairs.restype = ctypes.c_int
+_lib.ekv_pack_base_pairs.argtypes = [ctypes.POINTER(PagedKV), _vp, _vp, _vp, _i32, _vp]
 _lib.ekv_gather_compact_pages.restype = ctypes.c_int
 _lib.ekv_gather_compact_pages.argtypes = [ctypes.POINTER(PagedKV), _vp, _i32, _i32, _vp, _vp, _i32, _vp]
 _lib.ekv_prefill_attention.restype = ctypes.c_int
@@ -177,6 +185,36 @@ def ekv_decode_attention(kv: PagedKV, q: torch.Tensor, page_table: torch.Tensor,
         _ptr(fidelity), _ptr(seq_lens), int(max_seq_len), float(sm_scale), _ptr(out),
         _dtype_code(out), _ptr(lse), int(pages_per_split), _ptr(scratch),
         scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def ekv_decode_attention_elastic(kv: PagedKV, q: torch.Tensor, page_table: torch.Tensor,
+                                 fidelity: Optional[torch.Tensor], base_bounds: Optional[torch.Tensor],
+                                 has_base: bool, seq_lens: torch.Tensor, max_seq_len: int,
+                                 sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                                 scratch: Optional[torch.Tensor] = None, pages_per_split: int = 0,
+                                 stream=None) -> None:
+    """Decode over TARGET / compact / ElasticKV BASE pages (see ekv.h): per-page flags
+    (0, 1, 2) or per-sequence BASE bounds [B, 2] for TARGET-BASE-TARGET layouts."""
+    batch, hq, _ = q.shape
+    if scratch is None:
+        need = ekv_decode_scratch_bytes(batch, hq, kv.num_kv_heads, kv.head_dim, max_seq_len,
+                                        pages_per_split)
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.ekv_decode_attention_elastic(
+        ctypes.byref(kv), _ptr(q), batch, hq, _ptr(page_table), int(page_table.shape[1]),
+        _ptr(fidelity), _ptr(base_bounds), 1 if has_base else 0, _ptr(seq_lens), int(max_seq_len),
+        float(sm_scale), _ptr(out), _dtype_code(out), _ptr(lse), int(pages_per_split), _ptr(scratch),
+        scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def ekv_pack_base_pairs(kv: PagedKV, src_a: torch.Tensor, src_b: torch.Tensor, dst: torch.Tensor,
+                        stream=None) -> None:
+    """Pack TARGET block pairs into BASE blocks in the TARGET pools (see ekv.h)."""
+    for t in (src_a, src_b, dst):
+        if t.dtype != torch.int32:
+            raise TypeError("src_a, src_b and dst must be int32")
+    _check(_lib.ekv_pack_base_pairs(ctypes.byref(kv), _ptr(src_a), _ptr(src_b), _ptr(dst),
+                                    int(dst.shape[0]), _stream(stream)))
 
 
 def ekv_gather_compact_pages(kv: PagedKV, page_ids: torch.Tensor, apply_scale: bool,

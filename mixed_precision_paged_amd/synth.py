@@ -390,3 +390,65 @@ def writer_prefill_case(seed: int = 4, prompts: int = 32, length: int = 8192) ->
     """The compact-prefill prompt set (32 x 8192 tokens, 8 KV heads, D 128) written
     into 16,384 compact pages of a 17,408-page pool."""
     return make_writer_case(seed, [length] * prompts, 8, 128)
+
+
+BASE = 2
+
+
+@dataclasses.dataclass
+class ElasticCase:
+    """A paged batch in which some logical page pairs are ElasticKV BASE pages."""
+
+    paged: PagedCase              # fidelity 0 / 1 / 2; a BASE id b = half b % 2 of TARGET block b // 2
+    base_bounds: np.ndarray       # int32 [B, 2]: BASE logical pages [lo, hi) (structured layouts)
+    structured: bool              # True: every sequence is TARGET-BASE-TARGET within base_bounds
+
+
+def make_elastic_case(seed: int, seq_lens: Sequence[int], num_q_heads: int, num_kv_heads: int,
+                      head_dim: int, sink_pages: int = 2, recent_pages: int = 32,
+                      structured: bool = True, base_pair_frac: float = 0.5,
+                      compact_frac: float = 0.0) -> ElasticCase:
+    """Start from a seeded paged batch (TARGET pages, plus compact ones if compact_frac > 0)
+    and demote logical pairs (2i, 2i+1) of full TARGET pages outside the protected sink
+    (first ``sink_pages``) and recent (last ``recent_pages``) pages: all of them when
+    ``structured`` (one BASE range per sequence), else each with probability
+    ``base_pair_frac``.  A demoted pair is stored as in a demotion packed in place: the
+    first page's TARGET block holds the high bytes of both pages (first half, second half)
+    and the second page's block is freed (filled with NaN, never read)."""
+    c = make_paged_case(seed, seq_lens, num_q_heads, num_kv_heads, head_dim,
+                        compact_frac=compact_frac)
+    rng = _rng(seed + 1)
+    lens = c.seq_lens.astype(np.int64)
+    B = lens.shape[0]
+    full = lens // PAGE_SIZE                       # full pages per sequence
+    bounds = np.zeros((B, 2), dtype=np.int32)
+    k_bytes = c.k_target.view(np.uint8).reshape(c.k_target.shape[0], 2, PAGE_SIZE, num_kv_heads, head_dim)
+    v_bytes = c.v_target.view(np.uint8).reshape(c.v_target.shape[0], 2, PAGE_SIZE, num_kv_heads, head_dim)
+    for b in range(B):
+        lo = (sink_pages + 1) // 2 * 2
+        hi = max(lo, (min(int(full[b]), int((lens[b] + PAGE_SIZE - 1) // PAGE_SIZE) - recent_pages)) // 2 * 2)
+        pairs = []
+        for j in range(lo, hi, 2):
+            if c.fidelity[b, j] != TARGET or c.fidelity[b, j + 1] != TARGET:
+                continue
+            if structured or rng.random() < base_pair_frac:
+                pairs.append(j)
+        if structured:
+            bounds[b] = (lo, hi) if pairs else (0, 0)
+        for j in pairs:
+            pa, pb = int(c.page_table[b, j]), int(c.page_table[b, j + 1])
+            hk = (c.k_target[pa].view(np.uint16) >> 8).astype(np.uint8), (c.k_target[pb].view(np.uint16) >> 8).astype(np.uint8)
+            hv = (c.v_target[pa].view(np.uint16) >> 8).astype(np.uint8), (c.v_target[pb].view(np.uint16) >> 8).astype(np.uint8)
+            k_bytes[pa, 0], k_bytes[pa, 1] = hk
+            v_bytes[pa, 0], v_bytes[pa, 1] = hv
+            c.k_target[pb].view(np.uint16)[...] = FP16_NAN_BITS
+            c.v_target[pb].view(np.uint16)[...] = FP16_NAN_BITS
+            c.page_table[b, j], c.page_table[b, j + 1] = 2 * pa, 2 * pa + 1
+            c.fidelity[b, j] = c.fidelity[b, j + 1] = BASE
+    return ElasticCase(paged=c, base_bounds=bounds, structured=structured)
+
+
+def elastic_decode_case(seed: int = 6, batch: int = 32, ctx: int = 8192) -> ElasticCase:
+    """B 32, context 8192, 32 q / 8 KV heads, D 128: TARGET attention-sink pair and recent
+    512 tokens, the middle 478 pages (239 pairs) BASE, structured layout."""
+    return make_elastic_case(seed, [ctx] * batch, 32, 8, 128, sink_pages=2, recent_pages=32)

@@ -22,7 +22,7 @@ def _declared():
 
 def test_every_declared_function_is_exported():
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(ekv._lib, n), n
     assert sorted(ekv.EXPORTED) == names
@@ -179,3 +179,29 @@ def test_paged_prefill_validation():
     assert _paged_prefill(_kv(n_t=5, n_c=5), fidelity=None) == ekv.EKV_ERR_INVALID_ARG
     assert _paged_prefill(None) == ekv.EKV_ERR_INVALID_ARG
     assert _paged_prefill(kv, max_len=0) == ekv.EKV_OK
+
+
+def _elastic(kv, fidelity=FAKE, bounds=None, has_base=1):
+    return ekv._lib.ekv_decode_attention_elastic(ctypes.byref(kv), FAKE, 4, 32, FAKE, 512, fidelity, bounds,
+                                                 has_base, FAKE, 8192, 0.088, FAKE, 0, None, 0, FAKE,
+                                                 1 << 30, None)
+
+
+def test_elastic_decode_validation():
+    kv = _kv(n_t=64, n_c=0)
+    assert _elastic(kv, fidelity=FAKE, bounds=FAKE) == ekv.EKV_ERR_INVALID_ARG      # both given
+    assert _elastic(kv, fidelity=None, bounds=None) == ekv.EKV_ERR_INVALID_ARG      # neither given
+    assert _elastic(_kv(n_t=0, n_c=8), fidelity=FAKE) == ekv.EKV_ERR_INVALID_ARG   # no TARGET pool
+    assert _elastic(kv, fidelity=None, bounds=FAKE, has_base=0) == ekv.EKV_ERR_INVALID_ARG
+    assert _elastic(kv, has_base=2) == ekv.EKV_ERR_INVALID_ARG
+    assert _elastic(_kv(n_t=1 << 28, n_c=0)) == ekv.EKV_ERR_UNSUPPORTED
+
+
+def test_pack_validation():
+    f = ekv._lib.ekv_pack_base_pairs
+    kv = _kv(n_t=64, n_c=0)
+    assert f(ctypes.byref(_kv(n_t=0, n_c=5)), FAKE, FAKE, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(kv), None, FAKE, FAKE, 4, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(kv), FAKE, FAKE, FAKE, -1, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(_kv(hkv=32, n_t=64, n_c=0)), FAKE, FAKE, FAKE, 4, None) == ekv.EKV_ERR_UNSUPPORTED
+    assert f(ctypes.byref(kv), FAKE, FAKE, FAKE, 0, None) == ekv.EKV_OK

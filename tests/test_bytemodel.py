@@ -77,3 +77,18 @@ def test_writer_bytes_closed_forms():
     rd1, wr1 = bytemodel.quantize_bytes([5], 2, 64)
     assert rd1 == 5 * 2 * 64 * 4 + 12 and wr1 == 16 * 2 * 64 * 3 + 2 * 4
     assert bytemodel.append_bytes(32, 8, 128) == (32 * (4096 + 4), 32 * 4096)
+
+
+def test_base_pages_move_half_the_target_bytes():
+    """A BASE page moves 1 B of K and 1 B of V per element, no scale: half a TARGET page."""
+    H, D = 8, 128
+    lens = np.array([32])
+    t = bytemodel.decode_bytes(lens, np.array([[0, 0]]), 32, H, D, flags_read=False)
+    b = bytemodel.decode_bytes(lens, np.array([[2, 2]]), 32, H, D, flags_read=False)
+    c = bytemodel.decode_bytes(lens, np.array([[1, 1]]), 32, H, D, flags_read=False)
+    pairs = 32 * H * D
+    assert t - b == 2 * pairs                     # 4 B vs 2 B per K/V pair
+    assert c - b == pairs + 2 * H * 4             # 3 B vs 2 B per pair, plus the compact scales
+    s = bytemodel.decode_bytes(lens, np.array([[2, 2]]), 32, H, D, flags_read=False, bounds_read=True)
+    assert s - b == 8
+    assert bytemodel.pack_bytes(10, H, D) == (10 * (4 * 16 * H * D * 2 + 12), 10 * 2 * 16 * H * D * 2)

@@ -205,3 +205,22 @@ def test_paged_prefill_32x8192_one_launch():
                                                 cu_sub, True, c.sm_scale, rows=rows_sub)
     assert_close(got, want[rows_sub], what="paged prefill rows")
     assert_lse_close(glse, wlse[rows_sub])
+
+
+def test_elastic_decode_b32_ctx8192_structured():
+    """ElasticKV layout at full size (sink pair + 512 recent tokens TARGET, the middle BASE):
+    the structured path in the bench's launch, every output against the oracle."""
+    step("fullsize elastic decode B=32 ctx 8192, structured TARGET-BASE-TARGET")
+    e = synth.elastic_decode_case(seed=6)
+    c = e.paged
+    kv = ekv().paged_kv(c.num_kv_heads, c.head_dim, dev(c.k_target), dev(c.v_target))
+    pps = ekv().ekv_decode_plan_pages_per_split(c.seq_lens, c.num_kv_heads)
+    out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((c.batch, c.num_q_heads), dtype=torch.float32, device="cuda")
+    ekv().ekv_decode_attention_elastic(kv, dev(c.q), dev(c.page_table), None, dev(e.base_bounds), True,
+                                       dev(c.seq_lens), c.max_seq_len, c.sm_scale, out, lse,
+                                       pages_per_split=pps)
+    torch.cuda.synchronize()
+    want, wlse = oracle_decode(c)
+    assert_close(out.cpu().numpy(), want)
+    assert_lse_close(lse.cpu().numpy(), wlse)

@@ -192,7 +192,7 @@ def test_compact_page_with_exact_values_equals_target_page():
 
 def test_invalid_fidelity_flag_rejected():
     q, keys, vals16, codes, scales, flags, pools = _random_batch(1, [5], 2, 1, 4)
-    pools["fidelity"][0, 0] = 2
+    pools["fidelity"][0, 0] = 3   # 0, 1, 2 are TARGET, COMPACT, BASE
     with pytest.raises(ValueError):
         _decode(q, pools, 0.5)
 

@@ -136,3 +136,16 @@ def test_demote_with_pack_kernel_then_decode():
                                          c.seq_lens, c.sm_scale)
     assert_close(out.cpu().numpy(), want)
     assert_lse_close(lse.cpu().numpy(), wlse)
+
+
+def test_bypass_and_forced_general_path_agree_on_target_batch():
+    """A TARGET-only batch gives the same bits through the native path (indicator 0, no
+    flags) and forced through the general elastic path (indicator 1, all-TARGET flags)."""
+    step("bypass vs forced general path")
+    c = synth.make_paged_case(83, [1500, 700, 3000], 16, 4, 128, compact_frac=0.0)
+    out_n, lse_n = _elastic_decode(c, flags=False, has_base=False)
+    out_g, lse_g = _elastic_decode(c, flags=True, has_base=True)
+    assert np.array_equal(out_n.view(np.uint32), out_g.view(np.uint32))
+    assert np.array_equal(lse_n.view(np.uint32), lse_g.view(np.uint32))
+    want, wlse = _oracle(c)
+    assert_close(out_n, want)

@@ -52,3 +52,19 @@ def test_deterministic():
 
 def test_compact_decode_pool_size():
     assert synth._pool_size(16384, None, 0.0625) == 17408
+
+
+def test_elastic_case_bounds_match_flags_and_pairs():
+    """Structured layouts: flags are BASE exactly on [lo, hi) (pair-aligned, outside the
+    protected sink and recent pages); a BASE pair (2i, 2i+1) names both halves of one block."""
+    e = synth.make_elastic_case(3, [100, 600, 40, 333], 8, 2, 64, sink_pages=2, recent_pages=4)
+    c = e.paged
+    for b in range(c.batch):
+        n = (int(c.seq_lens[b]) + 15) // 16
+        lo, hi = (int(x) for x in e.base_bounds[b])
+        want = np.zeros(n, np.uint8)
+        want[lo:hi] = synth.BASE
+        assert np.array_equal(c.fidelity[b, :n], want)
+        assert lo % 2 == 0 and hi % 2 == 0 and (hi == 0 or (lo >= 2 and hi <= n - 4))
+        for j in range(lo, hi, 2):
+            assert c.page_table[b, j + 1] == c.page_table[b, j] + 1 and c.page_table[b, j] % 2 == 0

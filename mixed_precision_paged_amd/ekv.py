@@ -139,15 +139,18 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 def paged_kv(num_kv_heads: int, head_dim: int, k_target=None, v_target=None, k_compact=None,
              v_compact=None, v_scale=None) -> PagedKV:
-    """Descriptor of one layer's page pools (tensors stay owned by the caller)."""
+    """Descriptor of one layer's page pools.  The descriptor holds references to the
+    tensors whose device pointers it carries, so they live at least as long as it does."""
     n_t = int(k_target.shape[0]) if k_target is not None else 0
     n_c = int(k_compact.shape[0]) if k_compact is not None else 0
     for t, dt in ((k_target, torch.float16), (v_target, torch.float16), (k_compact, torch.float16),
                   (v_compact, torch.uint8), (v_scale, torch.float32)):
         if t is not None and t.dtype != dt:
             raise TypeError(f"pool tensor has dtype {t.dtype}, expected {dt}")
-    return PagedKV(_ptr(k_target), _ptr(v_target), n_t, _ptr(k_compact), _ptr(v_compact),
+    desc = PagedKV(_ptr(k_target), _ptr(v_target), n_t, _ptr(k_compact), _ptr(v_compact),
                    _ptr(v_scale), n_c, num_kv_heads, head_dim, PAGE_SIZE)
+    desc._tensors = (k_target, v_target, k_compact, v_compact, v_scale)
+    return desc
 
 
 def ekv_decode_pages_per_split(batch: int, num_kv_heads: int, max_seq_len: int) -> int:

@@ -205,3 +205,18 @@ def test_pack_validation():
     assert f(ctypes.byref(kv), FAKE, FAKE, FAKE, -1, None) == ekv.EKV_ERR_INVALID_ARG
     assert f(ctypes.byref(_kv(hkv=32, n_t=64, n_c=0)), FAKE, FAKE, FAKE, 4, None) == ekv.EKV_ERR_UNSUPPORTED
     assert f(ctypes.byref(kv), FAKE, FAKE, FAKE, 0, None) == ekv.EKV_OK
+
+
+def test_descriptor_keeps_its_tensors_alive():
+    """paged_kv(...) on temporaries must not leave dangling device pointers."""
+    import gc
+    import weakref
+
+    import torch
+
+    t = torch.zeros((2, 16, 1, 64), dtype=torch.float16)
+    ref = weakref.ref(t)
+    kv = ekv.paged_kv(1, 64, t, t.clone())
+    del t
+    gc.collect()
+    assert ref() is not None and kv._tensors[0] is ref()

@@ -3,8 +3,9 @@
 Headline workload: compact decode, batch 32, context 8192, 32 query / 8 KV
 heads, head dim 128, 16-token pages, FP16 K + E4M3 V with per-page-head fp32
 scales, seeded synthetic N(0,1) data, page table a random permutation of a
-17,408-page pool.  One step = one ekv_decode_attention call (split-K kernel +
-merge kernel) over the whole batch, with the per-page fidelity flags read.
+17,408-page pool.  One step = one ekv_decode_attention call over the whole
+batch (one split per sequence and KV head: the split kernel writes the
+output), with the per-page fidelity flags read.
 
 Prints ONE JSON line: decode HBM GB/s (algorithmic bytes / step time), with
 tokens/s, a roofline object for the decode call and the CPU oracle timed on
@@ -143,6 +144,7 @@ def main():
     value = algo_bytes / (ms_per_step * 1e-3) / 1e9
     kernel_ms = float(per_call_ms.mean())
     achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
+    single_split = -(-int(case.max_seq_len) // 16) <= pps
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -174,12 +176,13 @@ def main():
         "algorithmic_bytes_per_step": int(algo_bytes),
         "roofline": {
             "bound": "hbm",
-            "kernel": "ekv_decode_attention (decode_splitk_kernel + decode_merge_kernel)",
+            "kernel": ("ekv_decode_attention (decode_splitk_kernel, one split per sequence)" if single_split
+                       else "ekv_decode_attention (decode_splitk_kernel + decode_merge_kernel)"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": counted_traffic() if (fl is not None and pps == 256) else None,
+            "traffic": counted_traffic(pps) if fl is not None else None,
             "avg_call_us": round(kernel_ms * 1e3, 2),
         },
         "cpu_baseline": cpu,
@@ -547,9 +550,10 @@ def bench_elastic(args):
     print(json.dumps(line), flush=True)
 
 
-def counted_traffic():
+def counted_traffic(pps):
     """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, or None when the decode kernel sources changed since it was taken."""
+    summary, or None when the decode kernel sources or the split plan changed since
+    it was taken."""
     import hashlib
     import re
 
@@ -562,7 +566,8 @@ def counted_traffic():
         h = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()
     except (OSError, AttributeError, ValueError):
         return None
-    return int(rec["traffic_bytes_per_call"]) if rec.get("kernel_sources_sha256") == h else None
+    same = rec.get("kernel_sources_sha256") == h and rec.get("pages_per_split") == pps
+    return int(rec["traffic_bytes_per_call"]) if same else None
 
 
 def cpu_baseline(case, algo_bytes, min_seconds):

@@ -116,8 +116,9 @@ int32_t ekv_decode_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t 
 /*
  * Decode split plan from HOST-side sequence lengths (int32 [batch], host
  * memory), for callers whose scheduler knows them: batches of near-equal
- * lengths get one balanced round of about 512 workgroups; ragged batches get
- * smaller splits that balance the tail.  Pass the result as
+ * lengths get one balanced round (one split per sequence and KV head when
+ * there are 192..256 or at least 512 such groups, else about 512 split
+ * workgroups); ragged batches get smaller splits that balance the tail.  Pass the result as
  * `pages_per_split`.  Pure host function; NULL or empty input returns 16.
  */
 int32_t ekv_decode_plan_pages_per_split(const int32_t* seq_lens_host, int32_t batch,
@@ -125,7 +126,9 @@ int32_t ekv_decode_plan_pages_per_split(const int32_t* seq_lens_host, int32_t ba
 
 /*
  * Scratch bytes ekv_decode_attention needs for these sizes (split-K partial
- * results).  `pages_per_split` 0 = the automatic plan.  Pure host function.
+ * results).  `pages_per_split` 0 = the automatic plan.  0 when the plan has
+ * a single split per sequence: the output is then written without partials
+ * and scratch may be NULL.  Pure host function.
  */
 size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_seq_len, int32_t pages_per_split);
@@ -160,6 +163,7 @@ size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_
  *   pages_per_split  split-K granularity (0 = automatic; else 1..512).
  *   scratch    device buffer of at least ekv_decode_scratch_bytes(...) bytes
  *              (same arguments), 256-byte aligned; contents are overwritten.
+ *              Unused (may be NULL) when that size is 0.
  * Sequences that reference an out-of-range page id or an unknown flag get
  * NaN outputs and NaN lse.
  */

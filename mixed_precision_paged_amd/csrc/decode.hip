@@ -11,26 +11,28 @@
 // software, advance the online softmax tile by tile.
 //
 // Work decomposition (HBM-bound: every K/V byte is read exactly once):
-//   workgroup = (split of C pages, KV head g, sequence b); 4 wavefronts take
-//   the split's pages round-robin.  Inside a wavefront a page is 16 tokens x
-//   D: lane = (token pair tp = lane/8 -> tokens tp, tp+8; d-octet j = lane%8).
-//   Lane j owns d in {64c + 8j + e : c < D/64, e < 8}, so each 16-byte load
-//   instruction covers 8 token rows x 128 contiguous bytes.
-//   QK^T: v_dot2_f32_f16 over the lane's d (fp32 accumulate), then a 3-step
-//   DPP sum across the octet.  The G = Hq/Hkv query heads of the group share
-//   every K/V load.
-//   Softmax: online, per token-pair group (8 groups per wavefront), in log2
-//   units; the running max is raised only when a page max exceeds it by more
-//   than kTau (exact: softmax is shift invariant; it only skips rescales).
-//   PV: fp32 p times the fp16 value, fp32 accumulate (v_fma_mix_f32).
+//   workgroup = (split of pages, KV head g, sequence b); its wavefronts take
+//   the split's pages round-robin, one page (16 tokens x D) at a time, with
+//   the next page's loads in flight while the current one computes.  Page
+//   ids and flags of the split are staged in LDS once.  Loads go through a
+//   buffer descriptor that spans exactly one page of one KV head.
+//   QK^T: v_mfma_f32_16x16x32_f16 computes S^T = K Q^T with the page's 16
+//   tokens as rows and the G = Hq/Hkv query heads as columns (padded to 16),
+//   so the G heads share every K/V load.
+//   Softmax: online, in log2 units; the running max is raised only when a
+//   page max exceeds it by more than kTau (exact: softmax is shift invariant;
+//   it only skips rescales).
+//   PV: the scores are the A operand of v_mfma_f32_16x16x16f16 with V as B;
+//   P goes in as an fp16 hi + lo pair (two MFMAs), p = hi + lo to ~22 bits.
 //   Compact pages expand their E4M3 bytes in registers with the gfx950
 //   scaled conversion by the power-of-two part 2^e of the page-head scale
 //   (exact: code * 2^e is an fp16 value); the mantissa part f of the scale
-//   multiplies p in fp32.  Both kinds meet in one fp16-value PV path.  The flag is per page, so the
-//   branch is wavefront-uniform.
-//   End of split: groups merge by shuffles, wavefronts through LDS; the split
-//   writes (max, sum, unnormalized acc) partials.  The merge kernel combines
-//   splits: M = max m_s, L = sum l_s 2^(m_s-M), o = sum acc_s 2^(m_s-M) / L,
+//   multiplies p in fp32.  Both kinds meet in one fp16-value PV path.  The
+//   flag is per page, so the branch is wavefront-uniform.
+//   End of split: wavefronts merge through LDS.  One split per sequence: the
+//   workgroup writes the normalized output and LSE.  Several: it writes
+//   (max, sum, unnormalized acc) partials and the merge kernel combines them:
+//   M = max m_s, L = sum l_s 2^(m_s-M), o = sum acc_s 2^(m_s-M) / L,
 //   lse = (M + log2 L) ln 2.
 #include "ekv_device.hpp"
 #include "ekv_internal.hpp"
@@ -38,8 +40,6 @@
 namespace ekv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 constexpr float kTau = 8.0f;          // deferred-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;   // "no token yet" running max
 constexpr bool kHeadMajorGrid = true; // launch order: the KV heads of one (sequence, split) adjacent
@@ -281,13 +281,30 @@ __device__ __forceinline__ void process_page(State<D, G>& st, PageRegs<D>& r, co
   }
 }
 
+// Output rows of the G query heads of KV head g in sequence b when the
+// sequence is empty: out 0, lse -inf (single-split launches only).
+template <int D, int G>
+__device__ void write_empty_rows(const DecodeParams& p, int b, int g) {
+  const int64_t row0 = (int64_t)b * p.num_q_heads + g * G;
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    if (p.out_f32) static_cast<float*>(p.out)[row0 * D + i] = 0.f;
+    else static_cast<f16*>(p.out)[row0 * D + i] = (f16)0.f;
+  }
+  if (p.lse && (int)threadIdx.x < G) p.lse[row0 + threadIdx.x] = -__builtin_inff();
+}
+
 // MODE 0: every page has kind p.uniform_kind (no flag table); 1: per-page flags
 // TARGET/COMPACT; 2: per-page flags that may also be BASE (the batch-level
 // BASE indicator is set); 3: structured TARGET-BASE-TARGET layout: logical
 // pages [base_bounds[b][0], base_bounds[b][1]) of sequence b are BASE, all
 // others TARGET, with no flag table.
-template <int D, int G, int MODE>
-__global__ __launch_bounds__(kThreads, kMinWaves) void decode_splitk_kernel(DecodeParams p) {
+// NW wavefronts per workgroup.  DIRECT (one split per sequence, p.n_splits
+// == 1): the workgroup normalizes its result and writes out / lse itself, and
+// no merge kernel runs.
+template <int D, int G, int MODE, int NW, bool DIRECT>
+__global__ __launch_bounds__(NW * kWave, kMinWaves) void decode_splitk_kernel(DecodeParams p) {
+  constexpr int kThreads = NW * kWave;
+  constexpr int kWaves = NW;
   constexpr bool FLAGS = MODE == 1 || MODE == 2;
   constexpr bool HAS_BASE = MODE >= 2;
   constexpr int KBITS = HAS_BASE ? 2 : 1;  // kind bits in the staged page metadata
@@ -307,7 +324,10 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void decode_splitk_kernel(Deco
   const int len = min(max(p.seq_lens[b], 0), p.max_seq_len);
   const int npages = (len + kPage - 1) / kPage;
   const int pbeg = split * p.pages_per_split;
-  if (pbeg >= npages) return;  // the merge ignores splits past the sequence end
+  if (pbeg >= npages) {  // the merge ignores splits past the sequence end
+    if (DIRECT) write_empty_rows<D, G>(p, b, g);  // len 0: out 0, lse -inf
+    return;
+  }
   const int pend = min(pbeg + p.pages_per_split, npages);
 
   State<D, G> st;
@@ -444,10 +464,14 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void decode_splitk_kernel(Deco
   if (lane == 0) s_bad[wave] = bad ? 1 : 0;
   __syncthreads();
 
-  // Merge the wavefronts and write this split's partial result.
-  const bool anybad = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
+  // Merge the wavefronts; write this split's partial result, or (one split)
+  // the normalized output row and its LSE.
+  bool anybad = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) anybad |= s_bad[w] != 0;
   const float qnan = __builtin_nanf("");
   const int64_t slot = ((int64_t)(b * p.num_kv_heads + g) * p.n_splits + split) * G;
+  const int64_t row0 = (int64_t)b * p.num_q_heads + g * G;  // first output row of this group
   for (int i = threadIdx.x; i < G * D; i += kThreads) {
     const int h = i / D, d = i % D;
     float M = s_m[0][h];
@@ -456,9 +480,19 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void decode_splitk_kernel(Deco
     float o = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) o += s_acc[w][h][d] * fast_exp2(s_m[w][h] - M);
-    p.part_acc[(slot + h) * D + d] = anybad ? qnan : o;
+    if constexpr (DIRECT) {
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) L += s_l[w][h] * fast_exp2(s_m[w][h] - M);
+      const float v = anybad ? qnan : o * (1.0f / L);
+      if (p.out_f32) static_cast<float*>(p.out)[(row0 + h) * D + d] = v;
+      else static_cast<f16*>(p.out)[(row0 + h) * D + d] = (f16)v;
+      if (p.lse && d == 0) p.lse[row0 + h] = anybad ? qnan : (M + log2f(L)) * kLn2;
+    } else {
+      p.part_acc[(slot + h) * D + d] = anybad ? qnan : o;
+    }
   }
-  if (threadIdx.x < G) {
+  if (!DIRECT && threadIdx.x < G) {
     const int h = threadIdx.x;
     float M = s_m[0][h];
 #pragma unroll
@@ -531,19 +565,31 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeParams p) {
   if (p.lse && lane == 0) p.lse[row] = lse_v;
 }
 
+template <int D, int G, int NW, bool DIRECT>
+hipError_t launch_split(const DecodeParams& p, dim3 grid, hipStream_t stream) {
+  const int mode = p.has_base ? (p.fidelity ? 2 : 3) : (p.fidelity ? 1 : 0);
+  const dim3 block(NW * kWave);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 0, NW, DIRECT>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 1, NW, DIRECT>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 2, NW, DIRECT>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 3, NW, DIRECT>), grid, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid = kHeadMajorGrid ? dim3(p.num_kv_heads, p.n_splits, p.batch)
                                    : dim3(p.n_splits, p.num_kv_heads, p.batch);
+  if (p.n_splits == 1) {
+    // One split per sequence: the split kernel writes the output.  Up to 256
+    // (sequence, KV head) groups, 8 wavefronts per group keep 2 per SIMD.
+    return (int64_t)p.batch * p.num_kv_heads <= 256 ? launch_split<D, G, 8, true>(p, grid, stream)
+                                                     : launch_split<D, G, 4, true>(p, grid, stream);
+  }
   if (p.n_splits > 0) {
-    const int mode = p.has_base ? (p.fidelity ? 2 : 3) : (p.fidelity ? 1 : 0);
-    switch (mode) {
-      case 0: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 0>), grid, dim3(kThreads), 0, stream, p); break;
-      case 1: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 1>), grid, dim3(kThreads), 0, stream, p); break;
-      case 2: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 2>), grid, dim3(kThreads), 0, stream, p); break;
-      default: hipLaunchKernelGGL((decode_splitk_kernel<D, G, 3>), grid, dim3(kThreads), 0, stream, p); break;
-    }
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_split<D, G, 4, false>(p, grid, stream);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(p.num_q_heads, p.batch), dim3(kWave), 0, stream,
@@ -570,6 +616,10 @@ int32_t decode_auto_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t
   // multiples of the 4 wavefronts' page stride, between 16 and 512 pages.
   if (max_pages <= 0) return 16;
   const int64_t seqs = (int64_t)batch * num_kv_heads;
+  // 192..256 (sequence, KV head) groups: one split each in 8-wavefront
+  // workgroups fills the chip as well as two 4-wavefront splits would, and
+  // the split kernel writes the output itself (no partials, no merge launch).
+  if (seqs >= 192 && seqs <= 256 && max_pages <= kMaxSplitPages) return max_pages < 16 ? 16 : max_pages;
   int64_t c = (seqs * max_pages + 511) / 512;
   c = (c + 3) / 4 * 4;
   return (int32_t)(c < 16 ? 16 : (c > 512 ? 512 : c));
@@ -578,6 +628,7 @@ int32_t decode_auto_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t
 size_t decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t n_splits) {
   (void)num_kv_heads;
+  if (n_splits <= 1) return 0;  // one split writes the output directly
   const size_t rows = (size_t)batch * num_q_heads * (size_t)n_splits;  // (b, g, split, hh)
   const size_t acc = rows * head_dim * sizeof(float);
   const size_t acc_aligned = (acc + 255) & ~(size_t)255;

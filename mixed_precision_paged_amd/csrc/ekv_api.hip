@@ -158,7 +158,7 @@ ekv_status decode_impl(const ekv_paged_kv* kv, const void* q, int32_t batch, int
                                           : ekv_decode_pages_per_split(batch, kv->num_kv_heads, max_seq_len);
   const int32_t splits = max_pages > 0 ? ceil_div(max_pages, pps) : 0;
   const size_t need = ekv::decode_scratch_bytes(batch, num_q_heads, kv->num_kv_heads, kv->head_dim, splits);
-  if (splits > 0) {
+  if (need > 0) {  // more than one split: partial results go through scratch
     if (!scratch) return fail(EKV_ERR_INVALID_ARG, "scratch is NULL (%zu bytes needed)", need);
     if (((uintptr_t)scratch & 255u) != 0) return fail(EKV_ERR_INVALID_ARG, "scratch not 256-byte aligned");
     if (scratch_bytes < need) return fail(EKV_ERR_INVALID_ARG, "scratch of %zu bytes < %zu needed", scratch_bytes, need);
@@ -191,8 +191,8 @@ ekv_status decode_impl(const ekv_paged_kv* kv, const void* q, int32_t batch, int
   p.n_splits = splits;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   const size_t rows = (size_t)batch * num_q_heads * (size_t)splits;
-  p.part_acc = static_cast<float*>(scratch);
-  p.part_ml = splits > 0 ? reinterpret_cast<float*>(static_cast<char*>(scratch) +
+  p.part_acc = need > 0 ? static_cast<float*>(scratch) : nullptr;
+  p.part_ml = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(scratch) +
                                                     ((rows * kv->head_dim * sizeof(float) + 255) & ~(size_t)255))
                          : nullptr;
   p.out = out;

@@ -81,13 +81,18 @@ def test_decode_empty_batch_is_ok_without_launch():
 
 
 def test_split_plan_and_scratch_size():
-    pps = ekv.ekv_decode_pages_per_split(32, 8, 8192)
-    assert pps in (16, 32, 64, 128, 256, 512)
-    splits = -(-512 // pps)
-    rows = 32 * 32 * splits
-    acc = rows * 128 * 4
-    expect = ((acc + 255) // 256) * 256 + rows * 2 * 4
-    assert ekv.ekv_decode_scratch_bytes(32, 32, 8, 128, 8192, 0) == expect
+    # 256 (sequence, KV head) groups: one split each, no partials
+    assert ekv.ekv_decode_pages_per_split(32, 8, 8192) == 512
+    assert ekv.ekv_decode_scratch_bytes(32, 32, 8, 128, 8192, 0) == 0
+    for pps, splits in ((256, 2), (128, 4), (100, 6)):
+        rows = 32 * 32 * splits
+        acc = rows * 128 * 4
+        expect = ((acc + 255) // 256) * 256 + rows * 2 * 4
+        assert ekv.ekv_decode_scratch_bytes(32, 32, 8, 128, 8192, pps) == expect
+    # 128 groups: about 512 split workgroups of pages
+    assert ekv.ekv_decode_pages_per_split(16, 8, 8192) == 128
+    # 512 groups: one split each
+    assert ekv.ekv_decode_pages_per_split(64, 8, 8192) == 512
     assert ekv.ekv_decode_scratch_bytes(2, 4, 1, 64, 64, 1) == ((2 * 4 * 4 * 64 * 4 + 255) // 256) * 256 + 2 * 4 * 4 * 8
     assert ekv.ekv_decode_scratch_bytes(0, 4, 1, 64, 64, 1) == 0
 
@@ -95,7 +100,7 @@ def test_split_plan_and_scratch_size():
 def test_split_plan_from_host_lengths():
     import numpy as np
     uniform = ekv.ekv_decode_plan_pages_per_split(np.full(32, 8192), 8)
-    assert uniform == ekv.ekv_decode_pages_per_split(32, 8, 8192) == 256
+    assert uniform == ekv.ekv_decode_pages_per_split(32, 8, 8192) == 512
     lens = np.random.default_rng(0).integers(1024, 16385, size=64)
     ragged = ekv.ekv_decode_plan_pages_per_split(lens, 8)
     pages = int(((lens + 15) // 16).sum())

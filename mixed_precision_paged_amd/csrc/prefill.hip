@@ -53,10 +53,13 @@ constexpr int kXcds = 8;
 constexpr int kMaxPromptPages = 512;  // paged source: prompts of at most 8192 tokens
 
 template <int D>
-struct Smem {
+struct SmemK {
   static constexpr int kStride = D + 8;    // K row stride (halves): 16 B pad
-  static constexpr int vStride = kN + 4;   // V^T row stride (halves): 8 B pad
   f16 k[kN * kStride];
+};
+template <int D>
+struct SmemV {
+  static constexpr int vStride = kN + 4;   // V^T row stride (halves): 8 B pad
   f16 vt[D * vStride];
 };
 
@@ -77,9 +80,11 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 }
 
 template <int D>
-struct TileRegs {
+struct KRegs {
   static constexpr int KCH = kN * D / 8 / kThreads;  // 16-byte K chunks per thread
   uint4 k[KCH];
+};
+struct VRegs {
   uint2 vlo[4];  // 4 key rows x 8 d of one (key quad, d octet) unit: d 0..3 of
   uint2 vhi[4];  // each row in vlo, d 4..7 in vhi; for a compact page (paged
                  // source) vlo holds the row's 8 E4M3 codes and vhi is unused
@@ -110,14 +115,17 @@ __device__ __forceinline__ uint4 expand8(uint2 w, float s) {
 // prompt read as zeros (no per-load branch).  Per-lane byte offsets are fixed
 // for the whole loop; the tile's first row goes in the scalar offset.
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, __amdgpu_buffer_rsrc_t kr,
-                                          __amdgpu_buffer_rsrc_t vr, const uint32_t* koff,
-                                          const uint32_t* voff, uint32_t tile_off) {
+__device__ __forceinline__ void load_k(KRegs<D>& r, __amdgpu_buffer_rsrc_t kr, const uint32_t* koff,
+                                       uint32_t tile_off) {
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+  for (int i = 0; i < KRegs<D>::KCH; ++i) {
     const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], tile_off, 0);
     r.k[i] = make_uint4(x.x, x.y, x.z, x.w);
   }
+}
+
+__device__ __forceinline__ void load_v(VRegs& r, __amdgpu_buffer_rsrc_t vr, const uint32_t* voff,
+                                       uint32_t tile_off) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], tile_off, 0);
@@ -127,18 +135,23 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, __amdgpu_buffer_rsrc_t
   r.v_codes = false;
 }
 
-// Writes the staged tile to LDS: K row-major, V transposed.  The V unit
-// (key quad kq, d octet oc) of this thread holds keys 4kq..4kq+3, d 8oc..8oc+7.
-template <int D, bool SWZ>
-__device__ __forceinline__ void store_tile(Smem<D>& s, TileRegs<D>& r, int kq, int oc, bool v_active,
-                                           int valid_keys) {
+// Writes a staged K tile to LDS, row-major.
+template <int D>
+__device__ __forceinline__ void store_k(SmemK<D>& s, const KRegs<D>& r) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+  for (int i = 0; i < KRegs<D>::KCH; ++i) {
     const int idx = t + kThreads * i;
     const int key = idx / (D / 8), ch = idx % (D / 8);
-    *reinterpret_cast<uint4*>(&s.k[key * Smem<D>::kStride + 8 * ch]) = r.k[i];
+    *reinterpret_cast<uint4*>(&s.k[key * SmemK<D>::kStride + 8 * ch]) = r.k[i];
   }
+}
+
+// Writes a staged V tile to LDS transposed.  The V unit (key quad kq, d octet
+// oc) of this thread holds keys 4kq..4kq+3, d 8oc..8oc+7.
+template <int D, bool SWZ>
+__device__ __forceinline__ void store_v(SmemV<D>& s, const VRegs& r, int kq, int oc, bool v_active,
+                                        int valid_keys) {
   if (v_active) {
     uint4 v[4];
     // head dim 128: the page kind is wave-uniform (a branch); head dim 64: the
@@ -167,8 +180,8 @@ __device__ __forceinline__ void store_tile(Smem<D>& s, TileRegs<D>& r, int kq, i
       const uint2 odd = make_uint2(perm(r1[w], r0[w], 0x07060302u), perm(r3[w], r2[w], 0x07060302u));
       const int d = 8 * oc + 2 * w;
       const int kqs = kq ^ vt_swz<SWZ>(8 * oc);
-      *reinterpret_cast<uint2*>(&s.vt[d * Smem<D>::vStride + 4 * kqs]) = even;
-      *reinterpret_cast<uint2*>(&s.vt[(d + 1) * Smem<D>::vStride + 4 * kqs]) = odd;
+      *reinterpret_cast<uint2*>(&s.vt[d * SmemV<D>::vStride + 4 * kqs]) = even;
+      *reinterpret_cast<uint2*>(&s.vt[(d + 1) * SmemV<D>::vStride + 4 * kqs]) = odd;
     }
   }
 }
@@ -275,17 +288,16 @@ __device__ __forceinline__ void load_v_page(uint2* lo, uint2* hi, const PageDesc
   }
 }
 
-// Loads tile `it` (keys 64 it .. 64 it + 63 = prompt pages 4 it .. 4 it + 3).
+// Paged loads of tile t (keys 64 t .. 64 t + 63 = prompt pages 4 t .. 4 t + 3).
 // K chunk i of this thread lies in tile page D == 128 ? i : 2 i + wave / 2;
 // the V unit's page is the wavefront (D 128) or the half-wavefront (D 64).
 template <int D>
-__device__ __forceinline__ void load_tile_paged(TileRegs<D>& r, PagedSrc src, const TileMetaRaw& raw, int it,
-                                                int wave, int lane, uint32_t koff, uint32_t voff16,
-                                                uint32_t voff8) {
+__device__ __forceinline__ void load_k_paged(KRegs<D>& r, PagedSrc src, const TileMetaRaw& raw, int wave,
+                                             uint32_t koff) {
   const TileMeta tm = uniform_meta(raw);
   if constexpr (D == 128) {
 #pragma unroll
-    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+    for (int i = 0; i < KRegs<D>::KCH; ++i) {
       const PageDesc pd = page_desc(src, tm.m[i], tm.s[i]);
       const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pd.k, koff, 0, 0);
       r.k[i] = make_uint4(x.x, x.y, x.z, x.w);
@@ -293,12 +305,18 @@ __device__ __forceinline__ void load_tile_paged(TileRegs<D>& r, PagedSrc src, co
   } else {  // chunk i lies in page 2i + wave/2: a choice of two
     const bool hi = wave >> 1;
 #pragma unroll
-    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+    for (int i = 0; i < KRegs<D>::KCH; ++i) {
       const PageDesc pd = page_desc(src, hi ? tm.m[2 * i + 1] : tm.m[2 * i], hi ? tm.s[2 * i + 1] : tm.s[2 * i]);
       const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pd.k, koff, 0, 0);
       r.k[i] = make_uint4(x.x, x.y, x.z, x.w);
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v_paged(VRegs& r, PagedSrc src, const TileMetaRaw& raw, int wave, int lane,
+                                             uint32_t voff16, uint32_t voff8) {
+  const TileMeta tm = uniform_meta(raw);
   if constexpr (D == 128) {
     const PageDesc pd = page_desc(src, tm_meta(tm, wave), tm_scale(tm, wave));
     load_v_page(r.vlo, r.vhi, pd, src, voff16, voff8);
@@ -325,7 +343,7 @@ template <int D>
 __device__ void write_nan_rows(const PrefillParams& p, int64_t q0, int r_lo, int r_hi, int h) {
   const float qnan = __builtin_nanf("");
   const int64_t hq_row = (int64_t)p.num_q_heads * D;
-  for (int64_t i = threadIdx.x; i < (int64_t)(r_hi - r_lo) * D; i += kThreads) {
+  for (int64_t i = threadIdx.x; i < (int64_t)(r_hi - r_lo) * D; i += blockDim.x) {
     const int64_t rr = r_lo + i / D;
     const int64_t o = (q0 + rr) * hq_row + (int64_t)h * D + i % D;
     if (p.out_f32) static_cast<float*>(p.out)[o] = qnan;
@@ -338,7 +356,10 @@ template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, int n_mtiles) {
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  __shared__ Smem<D> sbuf[2];  // double buffer: tile i computes from one while i+1 is stored
+  // K of tiles i + 1 (computing S ahead) and i + 2 (being stored), V of
+  // tiles i (P.V) and i + 1 (being stored)
+  __shared__ SmemK<D> kbuf[2];
+  __shared__ SmemV<D> vbuf[2];
   // paged source: the prompt's page metadata for the tiles this workgroup reads
   __shared__ __attribute__((aligned(16))) int s_meta[PAGED ? kMaxPromptPages : 4];
   __shared__ __attribute__((aligned(16))) float s_scale[PAGED ? kMaxPromptPages : 4];
@@ -458,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   const int oc = PAGED ? vt_id % (D / 8) : vt_id / (kN / 4);
   __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, kBufferFlags);
   __amdgpu_buffer_rsrc_t vr = kr;
-  uint32_t koff[TileRegs<D>::KCH], voff[4];
+  uint32_t koff[KRegs<D>::KCH], voff[4];
   uint32_t pkoff = 0, pvoff16 = 0, pvoff8 = 0;
   if constexpr (PAGED) {
     // K chunk i: key t/(D/8) + (256/(D/8)) i, i.e. the same slot of tile page
@@ -474,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
     kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, span, kBufferFlags);
     vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, span, kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+    for (int i = 0; i < KRegs<D>::KCH; ++i) {
       const int idx = threadIdx.x + kThreads * i;
       koff[i] = (uint32_t)(idx / (D / 8)) * rowb + 16u * (idx % (D / 8));
     }
@@ -482,64 +503,69 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
     for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)(4 * kq + i) * rowb + 16u * oc;
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  TileRegs<D> tr;
-  tr.v_codes = false;
-  tr.vscale = 1.0f;
-  // paged source: metadata of the tile whose loads are issued next, read
-  // from LDS one iteration ahead
-  TileMetaRaw tmeta{};
-  if constexpr (PAGED) tmeta = read_tile_meta(s_meta, s_scale, 0);
-#define EKV_ISSUE_TILE(IT)                                                                      \
-  do {                                                                                          \
-    if constexpr (PAGED) {                                                                      \
-      load_tile_paged<D>(tr, src, tmeta, (IT), wave_u, lane, pkoff, pvoff16, pvoff8);           \
-      if ((IT) + 1 < n_tiles) tmeta = read_tile_meta(s_meta, s_scale, (IT) + 1);                \
-    } else {                                                                                    \
-      load_tile<D>(tr, kr, vr, koff, voff, (uint32_t)((IT) * kN) * rowb);                       \
-    }                                                                                           \
-  } while (0)
-  EKV_ISSUE_TILE(0);
-  store_tile<D, PAGED>(sbuf[0], tr, kq, oc, v_active, PAGED ? L : kN);
-  __syncthreads();
+  KRegs<D> kreg;
+  VRegs vreg;
+  vreg.v_codes = false;
+  vreg.vscale = 1.0f;
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const int n0 = it * kN;
-    Smem<D>& s = sbuf[it & 1];
-    // the next tile's loads are in flight while this tile computes
-    if (it + 1 < n_tiles) EKV_ISSUE_TILE(it + 1);
+  auto issue_k = [&](int t, const TileMetaRaw& tm) {
+    if constexpr (PAGED) load_k_paged<D>(kreg, src, tm, wave_u, pkoff);
+    else load_k<D>(kreg, kr, koff, (uint32_t)(t * kN) * rowb);
+  };
+  auto issue_v = [&](int t, const TileMetaRaw& tm) {
+    if constexpr (PAGED) load_v_paged<D>(vreg, src, tm, wave_u, lane, pvoff16, pvoff8);
+    else load_v(vreg, vr, voff, (uint32_t)(t * kN) * rowb);
+  };
+  auto meta = [&](int t) {
+    TileMetaRaw r{};
+    if constexpr (PAGED) r = read_tile_meta(s_meta, s_scale, t);
+    return r;
+  };
+  // Tiles 0 .. n_w - 1 hold keys this wavefront's rows can see (causal);
+  // the later ones are staged for the other wavefronts but not computed.
+  const int n_w = p.causal ? min(n_tiles, (r0 + 31) / kN + 1) : n_tiles;
 
-    if (!(p.causal && n0 > r0 + 31)) {  // skip tiles whose keys all follow this wavefront's rows
-
-    // S^T = K . Q^T for two 32-key blocks
-    f32x16 sacc[2];
+  // S^T = K . Q^T of one 32-key block of a tile (8 MFMAs over the head dim)
+  auto qk_block = [&](f32x16& sacc, const SmemK<D>& sk, int kb) {
+    sacc = f32x16{};
+    const f16* kp = &sk.k[(kb * 32 + col) * SmemK<D>::kStride + 8 * half];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      const f16* kp = &s.k[(kb * 32 + col) * Smem<D>::kStride + 8 * half];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(kp + 16 * ks);
-        sacc[kb] = mfma32(a, qb[ks], sacc[kb]);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      const f16x8 a = *reinterpret_cast<const f16x8*>(kp + 16 * ks);
+      sacc = mfma32(a, qb[ks], sacc);
     }
+  };
 
-    // mask (causal diagonal, prompt end) on the raw scores; the log2-unit scale
-    // is folded into the exponent's fma below (scale > 0 keeps the max)
-    const bool need_mask = (p.causal && n0 + kN - 1 > r0) || (n0 + kN > L);
-    float mx = -__builtin_inff();
+  // Causal diagonal / prompt-end mask on the raw scores of tile n0.
+  auto mask_tile = [&](f32x16 (&sacc)[2], int n0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = sacc[kb][r];
-        if (need_mask) {
-          const int key = n0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          const bool vis = key < L && (!p.causal || key <= qpos);
-          x = vis ? x : -__builtin_inff();
-        }
-        sacc[kb][r] = x;
-        mx = fmaxf(mx, x);
+        const int key = n0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+        const bool vis = key < L && (!p.causal || key <= qpos);
+        sacc[kb][r] = vis ? sacc[kb][r] : -__builtin_inff();
       }
+    }
+  };
+
+  // One compute step over tile t (scores CUR, already masked), with the
+  // scores of tile t + 1 (NXT) computed on the matrix cores in the same
+  // instruction stream: the running max of CUR interleaves with NXT's first
+  // key block, the exponentials with its second key block and the P.V MFMAs
+  // of CUR.  NXT may be garbage past the last computed tile (never used).
+  auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const SmemK<D>& sk, const SmemV<D>& sv) {
+    // running max (log2 units; scale > 0 keeps the max)
+    qk_block(nxt[0], sk, 0);
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
     }
     mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
     const float mnew = (mx > m + kTau) ? mx : m;
@@ -550,39 +576,81 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
       for (int i = 0; i < DB; ++i) oacc[i] *= a;
       m = mnew;
     }
-
+    qk_block(nxt[1], sk, 1);
     // P^T operand (fp16): PV k-block kk uses registers 8(kk%2)..+8 of block kk/2
-    f16x8 pb[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kk = 0; kk < 4; ++kk) {
+      f16x8 pb;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(__builtin_fmaf(sacc[kb][r], p.scale_log2, -m));
+      for (int r = 0; r < 8; ++r) {
+        const float pv = fast_exp2(__builtin_fmaf(cur[kk / 2][8 * (kk % 2) + r], p.scale_log2, -m));
         l += pv;
-        pb[kb * 2 + r / 8][r % 8] = (f16)pv;
+        pb[r] = (f16)pv;
       }
-    }
-
-    // O^T += V^T . P^T
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const f16* vp = &s.vt[(32 * db + col) * Smem<D>::vStride];
-      const int sw = vt_swz<PAGED>(32 * db + col);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int db = 0; db < DB; ++db) {
+        const f16* vp = &sv.vt[(32 * db + col) * SmemV<D>::vStride];
+        const int sw = vt_swz<PAGED>(32 * db + col);
         // key quads half + 4 kk (keys 16 kk + 4 half ..) and half + 4 kk + 2
         const uint2 lo = *reinterpret_cast<const uint2*>(vp + 4 * ((half + 4 * kk) ^ sw));
         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 4 * ((half + 4 * kk + 2) ^ sw));
         const uint4 a4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        oacc[db] = mfma32(__builtin_bit_cast(f16x8, a4), pb[kk], oacc[db]);
+        oacc[db] = mfma32(__builtin_bit_cast(f16x8, a4), pb, oacc[db]);
       }
     }
+#pragma unroll
+    for (int i = 0; i < KS + 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);  // three VALU
     }
-    // store the next tile into the other buffer; one barrier publishes it and
-    // guarantees every wavefront has finished reading the buffer it overwrites next
-    if (it + 1 < n_tiles) store_tile<D, PAGED>(sbuf[(it + 1) & 1], tr, kq, oc, v_active, PAGED ? L - n0 - kN : kN);
-    __syncthreads();
+  };
+
+  // Prologue: K(0), V(0), K(1) into LDS, then S(0).  Paged source: tile
+  // metadata is read from LDS one iteration before its loads are issued;
+  // tmk belongs to the next K tile, tmv to the next V tile.
+  TileMetaRaw tmk = meta(0), tmv{};
+  issue_k(0, tmk);
+  issue_v(0, tmk);
+  store_k<D>(kbuf[0], kreg);
+  store_v<D, PAGED>(vbuf[0], vreg, kq, oc, v_active, PAGED ? L : kN);
+  if (n_tiles > 1) {
+    tmv = meta(1);
+    issue_k(1, tmv);
+    store_k<D>(kbuf[1], kreg);
   }
+  if (n_tiles > 2) tmk = meta(2);
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  qk_block(sA[0], kbuf[0], 0);
+  qk_block(sA[1], kbuf[0], 1);
+
+  // Iteration t: loads of K(t+2) and V(t+1) are in flight while S(t+1) is
+  // computed on the matrix cores and the softmax of S(t) runs on the vector
+  // ALUs, then O += V(t) P(t); the staged tiles go to the buffers freed by
+  // K(t) and V(t-1), and one barrier publishes them.
+#define EKV_PREFILL_STEP(CUR, NXT)                                                              \
+  {                                                                                             \
+    if (it + 2 < n_tiles) issue_k(it + 2, tmk);                                                 \
+    if (it + 1 < n_tiles) issue_v(it + 1, tmv);                                                 \
+    if constexpr (PAGED) {                                                                      \
+      tmv = tmk;                                                                                \
+      if (it + 3 < n_tiles) tmk = meta(it + 3);                                                 \
+    }                                                                                           \
+    if (it < n_w) {                                                                             \
+      if ((p.causal && it * kN + kN - 1 > r0) || (it * kN + kN > L)) mask_tile(CUR, it * kN);   \
+      step(CUR, NXT, kbuf[(it + 1) & 1], vbuf[it & 1]);                                         \
+    }                                                                                           \
+    if (it + 2 < n_tiles) store_k<D>(kbuf[it & 1], kreg);                                       \
+    if (it + 1 < n_tiles)                                                                       \
+      store_v<D, PAGED>(vbuf[(it + 1) & 1], vreg, kq, oc, v_active, PAGED ? L - (it + 1) * kN : kN); \
+    __syncthreads();                                                                            \
+    if (++it >= n_tiles) break;                                                                 \
+  }
+  for (int it = 0; it < n_tiles;) {
+    EKV_PREFILL_STEP(sA, sB)
+    EKV_PREFILL_STEP(sB, sA)
+  }
+#undef EKV_PREFILL_STEP
 
   // normalize and store rows of this lane's column
   l += shfl_xor(l, 32);
@@ -608,7 +676,259 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   if (p.lse && half == 0) p.lse[qrow * p.num_q_heads + h] = (m + log2f(l)) * kLn2;
 }
 
-#undef EKV_ISSUE_TILE
+// Head dim 128 over workspace rows: the same flash loop with the K and V
+// tiles staged by buffer loads straight into LDS (no staging registers, no
+// LDS stores) and V^T operands read with gfx950 transposing LDS reads.
+//   LDS tiles are row-major, 256 B per key row, 16-byte chunks swizzled:
+//   K chunk c of row r sits at chunk c ^ (r % 16): the 16 rows one
+//   ds_read_b128 pass touches hit 16 distinct bank groups.  V chunk c of row
+//   r sits at chunk c ^ 4 (r % 4): the 4 rows x 64 B one transposing read
+//   pass touches hit 16 distinct bank groups.
+//   Staging: each wavefront moves 4 K and 4 V row quads (1 KiB each) per
+//   tile; lane l writes bytes 16 l of its quad, i.e. row l / 16, swizzled
+//   chunk l % 16, so it loads the source chunk that belongs there.  Rows past
+//   the prompt are outside the descriptor range and arrive as zeros.
+//   V^T operand: ds_read_b64_tr_b16 returns, in lane j of each 16-lane group,
+//   element j % 4 of the 8-byte pieces addressed by lanes 4k + j / 4 (k =
+//   0..3); lane i of the group addresses key row key0 + i / 4 at d offset
+//   4 (i % 4), so lane j receives V[key0 + k][d0 + j] for k = 0..3: four keys
+//   of one d, the A-operand layout of O^T = V^T P^T.
+constexpr int kWsD = 128;
+constexpr int kWsWaves = 4;  // measured: 4 wavefronts (128 rows) beat 8 (256 rows) by 5%
+__host__ __device__ inline bool paged_route(const PrefillParams& p) { return p.page_table != nullptr; }
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, f16* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint2 lds_tr16(const f16* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// NW wavefronts, 32 NW query rows per workgroup, sharing every staged tile.
+template <int NW>
+__global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillParams p, int n_mtiles) {
+  constexpr int D = kWsD;
+  constexpr int QUADS = 16 / NW;  // K (and V) row quads each wavefront stages per tile
+  constexpr int KS = D / 16;  // k-steps of 16 over the head dim
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int TILE = kN * D;  // halves per K or V tile
+  // K of tiles t + 1 (computing S ahead) and t + 2 (being staged), V of
+  // tiles t (P.V) and t + 1 (being staged)
+  __shared__ __attribute__((aligned(1024))) f16 kbuf[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) f16 vbuf[2 * TILE];
+
+  // XCD-aware work mapping (as in prefill_kernel).
+  const int total = (int)(gridDim.x);
+  const int bid = blockIdx.x;
+  const int work = (total % kXcds == 0) ? (bid % kXcds) * (total / kXcds) + bid / kXcds : bid;
+  const int mt_rev = work % n_mtiles;
+  const int h = (work / n_mtiles) % p.num_q_heads;
+  const int prompt = work / (n_mtiles * p.num_q_heads);
+  const int mt = n_mtiles - 1 - mt_rev;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int g = h / G;
+
+  const int q0 = p.cu_seqlens_q[prompt];
+  const int q1 = p.cu_seqlens_q[prompt + 1];
+  if (q0 < 0 || q1 < q0 || q1 > p.q_rows) return;  // rows not addressable: nothing to write
+  const int L = q1 - q0;
+  const int m0 = mt * 32 * NW;
+  const int kv0 = p.kv_start[prompt];
+  const bool ok = L <= p.max_len && kv0 >= 0 && (int64_t)kv0 + L <= p.kv_rows;
+  if (!ok) {
+    if (mt == 0) write_nan_rows<D>(p, q0, 0, L, h);
+    return;
+  }
+  if (m0 >= L) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int r0 = m0 + 32 * wave;
+  const int qpos = r0 + col;
+  const int64_t qrow = (int64_t)q0 + qpos;
+  const int64_t hq_row = (int64_t)p.num_q_heads * D;
+  const int n_end = p.causal ? min(L, m0 + 32 * NW) : L;
+  const int n_tiles = (n_end + kN - 1) / kN;
+  const int n_w = p.causal ? min(n_tiles, (r0 + 31) / kN + 1) : n_tiles;
+  const uint32_t rowb = (uint32_t)p.num_kv_heads * D * 2u;
+
+  // descriptors over this prompt's K/V rows of KV head g
+  const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2u;
+  const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
+  const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, span, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, span, kBufferFlags);
+
+  // staging: row quad j of this wavefront = tile rows 4 (QUADS wave + j) .. + 3
+  uint32_t kso[QUADS], vso[QUADS];
+#pragma unroll
+  for (int j = 0; j < QUADS; ++j) {
+    const int r = 4 * (QUADS * wave + j) + (lane >> 4), pc = lane & 15;
+    kso[j] = (uint32_t)r * rowb + 16u * (uint32_t)(pc ^ (r & 15));
+    vso[j] = (uint32_t)r * rowb + 16u * (uint32_t)(pc ^ (4 * (r & 3)));
+  }
+  auto stage_k = [&](int t, int b) {
+    const uint32_t to = (uint32_t)(t * kN) * rowb;
+#pragma unroll
+    for (int j = 0; j < QUADS; ++j) lds_dma16(kr, &kbuf[b * TILE + 4 * (QUADS * wave + j) * D], kso[j] + to);
+  };
+  auto stage_v = [&](int t, int b) {
+    const uint32_t to = (uint32_t)(t * kN) * rowb;
+#pragma unroll
+    for (int j = 0; j < QUADS; ++j) lds_dma16(vr, &vbuf[b * TILE + 4 * (QUADS * wave + j) * D], vso[j] + to);
+  };
+
+  // QK^T A operand: K row kb*32 + col, chunk 2 ks + half at chunk (2 ks + half) ^ (col % 16)
+  uint32_t kro[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kro[ks] = (uint32_t)col * D + 8u * (uint32_t)((2 * ks + half) ^ (col & 15));
+  // V^T A operand (transposing reads): lane i = l % 16 of group q16 = l / 16
+  // addresses key row 4 (q16 / 2) + i / 4 (+ 16 kk, + 8 for the high keys)
+  // at d = 32 db + 16 (q16 % 2) + 4 (i % 4)
+  uint32_t vro[DB];
+  {
+    const int i = lane & 15, q16 = lane >> 4;
+    const int row = 4 * (q16 >> 1) + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = 4 * db + 2 * (q16 & 1) + ((i & 3) >> 1);
+      vro[db] = (uint32_t)row * D + 8u * (uint32_t)(c ^ (4 * (row & 3))) + 4u * (uint32_t)(i & 1);
+    }
+  }
+
+  // Q^T operand: lane holds Q[qpos][16ks + 8half .. +8] for each k-step.
+  f16x8 qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (qpos < L) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p.q + qrow * hq_row + (int64_t)h * D + 16 * ks + 8 * half);
+      qb[ks] = __builtin_bit_cast(f16x8, x);
+    } else {
+      qb[ks] = f16x8{};
+    }
+  }
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m = kNegBig, l = 0.f;
+
+  auto qk_block = [&](f32x16& sacc, int b, int kb) {
+    sacc = f32x16{};
+    const f16* kp = &kbuf[b * TILE + kb * 32 * D];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const f16x8 a = *reinterpret_cast<const f16x8*>(kp + kro[ks]);
+      sacc = mfma32(a, qb[ks], sacc);
+    }
+  };
+  auto mask_tile = [&](f32x16 (&sacc)[2], int n0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = n0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+        const bool vis = key < L && (!p.causal || key <= qpos);
+        sacc[kb][r] = vis ? sacc[kb][r] : -__builtin_inff();
+      }
+    }
+  };
+  auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int kb_buf, int vb_buf) {
+    qk_block(nxt[0], kb_buf, 0);
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+    mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
+    const float mnew = (mx > m + kTau) ? mx : m;
+    if (__ballot(mnew != m)) {
+      const float a = fast_exp2(m - mnew);
+      l *= a;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= a;
+      m = mnew;
+    }
+    qk_block(nxt[1], kb_buf, 1);
+    const f16* vt = &vbuf[vb_buf * TILE];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      f16x8 pb;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float pv = fast_exp2(__builtin_fmaf(cur[kk / 2][8 * (kk % 2) + r], p.scale_log2, -m));
+        l += pv;
+        pb[r] = (f16)pv;
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        // keys 16 kk + 4 half' + 0..3 (lo) and + 8 (hi) of d 32 db + col
+        const uint2 lo = lds_tr16(vt + vro[db] + 16 * kk * D);
+        const uint2 hi = lds_tr16(vt + vro[db] + (16 * kk + 8) * D);
+        const uint4 a4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        oacc[db] = mfma32(__builtin_bit_cast(f16x8, a4), pb, oacc[db]);
+      }
+    }
+  };
+
+  // Prologue: K(0), V(0), K(1) staged; then S(0).
+  stage_k(0, 0);
+  stage_v(0, 0);
+  if (n_tiles > 1) stage_k(1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's tile loads have landed
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  qk_block(sA[0], 0, 0);
+  qk_block(sA[1], 0, 1);
+
+  // Iteration t: K(t+2) and V(t+1) stream into LDS while S(t+1) runs on the
+  // matrix cores and the softmax of S(t) on the vector ALUs, then O += V(t)
+  // P(t); the staged tiles land in the buffers freed by K(t) and V(t-1).
+#define EKV_WS_STEP(CUR, NXT)                                                                   \
+  {                                                                                             \
+    if (it + 2 < n_tiles) stage_k(it + 2, it & 1);                                              \
+    if (it + 1 < n_tiles) stage_v(it + 1, (it + 1) & 1);                                        \
+    if (it < n_w) {                                                                             \
+      if ((p.causal && it * kN + kN - 1 > r0) || (it * kN + kN > L)) mask_tile(CUR, it * kN);   \
+      step(CUR, NXT, (it + 1) & 1, it & 1);                                                     \
+    }                                                                                           \
+    __builtin_amdgcn_s_waitcnt(0x0F70);                                                         \
+    __syncthreads();                                                                            \
+    if (++it >= n_tiles) break;                                                                 \
+  }
+  for (int it = 0; it < n_tiles;) {
+    EKV_WS_STEP(sA, sB)
+    EKV_WS_STEP(sB, sA)
+  }
+#undef EKV_WS_STEP
+
+  // normalize and store rows of this lane's column
+  l += shfl_xor(l, 32);
+  if (qpos >= L) return;
+  const float inv = 1.0f / l;
+  const int64_t obase = qrow * hq_row + (int64_t)h * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int d = 32 * db + 8 * rb + 4 * half;
+      const float o0 = oacc[db][4 * rb + 0] * inv, o1 = oacc[db][4 * rb + 1] * inv;
+      const float o2 = oacc[db][4 * rb + 2] * inv, o3 = oacc[db][4 * rb + 3] * inv;
+      if (p.out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + d) = f32x4{o0, o1, o2, o3};
+      } else {
+        f16x2 a, b;
+        a.x = (f16)o0; a.y = (f16)o1; b.x = (f16)o2; b.y = (f16)o3;
+        *reinterpret_cast<uint2*>(static_cast<f16*>(p.out) + obase + d) = make_uint2(bits(a), bits(b));
+      }
+    }
+  }
+  if (p.lse && half == 0) p.lse[qrow * p.num_q_heads + h] = (m + log2f(l)) * kLn2;
+}
 
 }  // namespace
 
@@ -617,11 +937,17 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const int n_mtiles = (p.max_len + kM - 1) / kM;
   const int64_t blocks = (int64_t)n_mtiles * p.num_q_heads * p.n_prompts;
   const dim3 grid((unsigned)blocks), block(kThreads);
+  if (p.head_dim == kWsD && !paged_route(p)) {
+    constexpr int NW = kWsWaves;
+    const int n_mt = (p.max_len + 32 * NW - 1) / (32 * NW);
+    const int64_t nb = (int64_t)n_mt * p.num_q_heads * p.n_prompts;
+    hipLaunchKernelGGL(prefill_ws128_kernel<NW>, dim3((unsigned)nb), dim3(NW * kWave), 0, stream, p, n_mt);
+    return hipGetLastError();
+  }
   const bool paged = p.page_table != nullptr;
   if (paged && p.max_len > kMaxPromptPages * kPage) return hipErrorInvalidValue;
-  if (p.head_dim == 128) {
-    if (paged) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, p, n_mtiles);
-    else hipLaunchKernelGGL((prefill_kernel<128, false>), grid, block, 0, stream, p, n_mtiles);
+  if (p.head_dim == 128 && paged) {
+    hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, p, n_mtiles);
   } else if (p.head_dim == 64) {
     if (paged) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, block, 0, stream, p, n_mtiles);
     else hipLaunchKernelGGL((prefill_kernel<64, false>), grid, block, 0, stream, p, n_mtiles);

@@ -525,23 +525,41 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeParams p) {
     lse_v = -__builtin_inff();
   } else {
     const int64_t base = (int64_t)(b * p.num_kv_heads + g) * p.n_splits;
+    // split statistics are spread over the lanes (split s in lane s % 64), so
+    // their loads and the max / sum reductions run in parallel
     float M = kNegBig;
     bool bad = false;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = p.part_ml[((base + s) * G + hh) * 2];
+    for (int s0 = 0; s0 < nsplit; s0 += kWave) {
+      const int s = s0 + lane;
+      const float ms = s < nsplit ? p.part_ml[((base + s) * G + hh) * 2] : kNegBig;
       bad |= ms != ms;
       M = fmaxf(M, ms);
     }
+#pragma unroll
+    for (int x = 1; x < kWave; x <<= 1) M = fmaxf(M, shfl_xor(M, x));
+    bad = __ballot(bad) != 0;
     float L = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const int64_t k = (base + s) * G + hh;
-      const float f = fast_exp2(p.part_ml[k * 2] - M);
-      L += p.part_ml[k * 2 + 1] * f;
+    for (int s0 = 0; s0 < nsplit; s0 += kWave) {
+      const int s = s0 + lane;
+      float f_lane = 0.f;
+      if (s < nsplit) {
+        const int64_t k = (base + s) * G + hh;
+        f_lane = fast_exp2(p.part_ml[k * 2] - M);
+        L += p.part_ml[k * 2 + 1] * f_lane;
+      }
+      const int cnt = min(kWave, nsplit - s0);
+#pragma unroll 4
+      for (int j = 0; j < cnt; ++j) {
+        const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f_lane), j));
+        const int64_t k = (base + s0 + j) * G + hh;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) o[i] += p.part_acc[k * D + lane + kWave * i] * f;
+        for (int i = 0; i < PER; ++i) o[i] += p.part_acc[k * D + lane + kWave * i] * f;
+      }
     }
+#pragma unroll
+    for (int x = 1; x < kWave; x <<= 1) L += shfl_xor(L, x);
     const float inv = 1.0f / L;
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] *= inv;

@@ -53,6 +53,7 @@ extern "C" {
 #define EKV_FIDELITY_BASE 2     /* ElasticKV BASE: high FP16 byte of K and V,
                                    two pages per TARGET block (elastic decode) */
 #define EKV_MAX_PREFILL_TOKENS 8192 /* [asym] route rule: prompts of at most 8,192 tokens */
+#define EKV_DECODE_BALANCED (-1)    /* decode plan: equal shares of all page-heads per workgroup */
 
 typedef enum {
   EKV_OK = 0,
@@ -118,7 +119,8 @@ int32_t ekv_decode_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t 
  * memory), for callers whose scheduler knows them: batches of near-equal
  * lengths get one balanced round (one split per sequence and KV head when
  * there are 192..256 or at least 512 such groups, else about 512 split
- * workgroups); ragged batches get smaller splits that balance the tail.  Pass the result as
+ * workgroups); ragged batches (up to 2,048 sequences) get
+ * EKV_DECODE_BALANCED, larger ragged ones small splits.  Pass the result as
  * `pages_per_split`.  Pure host function; NULL or empty input returns 16.
  */
 int32_t ekv_decode_plan_pages_per_split(const int32_t* seq_lens_host, int32_t batch,
@@ -160,7 +162,13 @@ size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_
  *              value is the round-to-nearest-even of the EKV_F32 result.
  *   lse        optional fp32 [batch][num_q_heads]: natural-log normalizer
  *              max_t s_t + ln sum_t exp(s_t - max_t s_t).
- *   pages_per_split  split-K granularity (0 = automatic; else 1..512).
+ *   pages_per_split  split-K granularity (0 = automatic; else 1..512), or
+ *              EKV_DECODE_BALANCED (batch <= 2,048): all page-heads of the
+ *              batch, ordered (sequence, KV head, page), are cut into equal
+ *              contiguous ranges, one per workgroup in a single round; a
+ *              sequence that one range holds whole is written directly, the
+ *              pieces of a cut one are merged by a second kernel.  Evens out
+ *              ragged lengths.
  *   scratch    device buffer of at least ekv_decode_scratch_bytes(...) bytes
  *              (same arguments), 256-byte aligned; contents are overwritten.
  *              Unused (may be NULL) when that size is 0.

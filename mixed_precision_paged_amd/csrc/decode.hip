@@ -44,6 +44,7 @@ constexpr float kTau = 8.0f;          // deferred-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;   // "no token yet" running max
 constexpr bool kHeadMajorGrid = true; // launch order: the KV heads of one (sequence, split) adjacent
 constexpr int kMaxSplitPages = 512;   // pages per split (metadata staged in LDS)
+constexpr int kBalancedRound = 512;   // balanced plan: workgroups per round
 constexpr int kSlots = 2;             // register page buffers per wavefront (pages in flight + 1)
 constexpr int kMinWaves = 2;          // occupancy bound (wavefronts per SIMD) for G*D < 1024
 
@@ -293,43 +294,36 @@ __device__ void write_empty_rows(const DecodeParams& p, int b, int g) {
   if (p.lse && (int)threadIdx.x < G) p.lse[row0 + threadIdx.x] = -__builtin_inff();
 }
 
+// LDS of one workgroup of NW wavefronts working on one piece of a sequence.
+template <int D, int G, int NW>
+struct PieceSmem {
+  float acc[NW][G][D];
+  float m[NW][G];
+  float l[NW][G];
+  int bad[NW];
+  int meta[kMaxSplitPages];
+};
+
 // MODE 0: every page has kind p.uniform_kind (no flag table); 1: per-page flags
 // TARGET/COMPACT; 2: per-page flags that may also be BASE (the batch-level
 // BASE indicator is set); 3: structured TARGET-BASE-TARGET layout: logical
 // pages [base_bounds[b][0], base_bounds[b][1]) of sequence b are BASE, all
 // others TARGET, with no flag table.
-// NW wavefronts per workgroup.  DIRECT (one split per sequence, p.n_splits
-// == 1): the workgroup normalizes its result and writes out / lse itself, and
-// no merge kernel runs.
-template <int D, int G, int MODE, int NW, bool DIRECT>
-__global__ __launch_bounds__(NW * kWave, kMinWaves) void decode_splitk_kernel(DecodeParams p) {
+//
+// Attention of the G query heads of KV head g of sequence b (length len) over
+// its logical pages [pbeg, pend) (at most kMaxSplitPages): the NW wavefronts
+// take the pages round-robin and leave their (max, sum, unnormalized acc) and
+// bad-page flags in sm, published by a barrier.  The caller must not reuse sm
+// before every wavefront has read what it needs (a barrier).
+template <int D, int G, int MODE, int NW>
+__device__ __forceinline__ void run_piece(const DecodeParams& p, PieceSmem<D, G, NW>& sm, int b, int g, int len,
+                                          int pbeg, int pend, int lane, int wave) {
   constexpr int kThreads = NW * kWave;
   constexpr int kWaves = NW;
   constexpr bool FLAGS = MODE == 1 || MODE == 2;
   constexpr bool HAS_BASE = MODE >= 2;
   constexpr int KBITS = HAS_BASE ? 2 : 1;  // kind bits in the staged page metadata
   constexpr int NE = D / 16;
-  __shared__ float s_acc[kWaves][G][D];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-  __shared__ int s_bad[kWaves];
-  __shared__ int s_meta[kMaxSplitPages];
-
-  const int lane = threadIdx.x & (kWave - 1);
-  // wavefront index made provably uniform, so page metadata becomes scalar loads
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int split = kHeadMajorGrid ? blockIdx.y : blockIdx.x;
-  const int g = kHeadMajorGrid ? blockIdx.x : blockIdx.y;
-  const int b = blockIdx.z;
-  const int len = min(max(p.seq_lens[b], 0), p.max_seq_len);
-  const int npages = (len + kPage - 1) / kPage;
-  const int pbeg = split * p.pages_per_split;
-  if (pbeg >= npages) {  // the merge ignores splits past the sequence end
-    if (DIRECT) write_empty_rows<D, G>(p, b, g);  // len 0: out 0, lse -inf
-    return;
-  }
-  const int pend = min(pbeg + p.pages_per_split, npages);
-
   State<D, G> st;
   {
     const int qh = lane & 15, qc = lane >> 4;
@@ -359,7 +353,7 @@ __global__ __launch_bounds__(NW * kWave, kMinWaves) void decode_splitk_kernel(De
       const bool ok = (kind == 0 && (unsigned)phys < (unsigned)p.n_target) ||
                       (kind == 1 && (unsigned)phys < (unsigned)p.n_compact) ||
                       (HAS_BASE && kind == 2 && (unsigned)phys < 2u * (unsigned)p.n_target);
-      s_meta[i] = ok ? (phys << KBITS) | kind : -1;
+      sm.meta[i] = ok ? (phys << KBITS) | kind : -1;
     }
   }
   __syncthreads();
@@ -377,12 +371,12 @@ __global__ __launch_bounds__(NW * kWave, kMinWaves) void decode_splitk_kernel(De
   auto issue = [&](Slot<D>& sl, int pq) {
     int m;
     if constexpr (HAS_BASE) {  // no early exit: a missing page issues range-0 loads
-      m = pq < pend ? __builtin_amdgcn_readfirstlane(s_meta[pq - pbeg]) : -2;
+      m = pq < pend ? __builtin_amdgcn_readfirstlane(sm.meta[pq - pbeg]) : -2;
       bad |= m == -1;
     } else {
       sl.ok = false;
       if (pq >= pend) return;
-      m = __builtin_amdgcn_readfirstlane(s_meta[pq - pbeg]);
+      m = __builtin_amdgcn_readfirstlane(sm.meta[pq - pbeg]);
       if (m < 0) { bad = true; return; }
     }
     sl.ok = m >= 0;
@@ -453,60 +447,198 @@ __global__ __launch_bounds__(NW * kWave, kMinWaves) void decode_splitk_kernel(De
       const int h = 4 * tq + i;
       if (h < G) {
 #pragma unroll
-        for (int e = 0; e < NE; ++e) s_acc[wave][h][NE * dq + e] = st.acc[e][i];
+        for (int e = 0; e < NE; ++e) sm.acc[wave][h][NE * dq + e] = st.acc[e][i];
       }
     }
     if (tq == 0 && dq < G) {
-      s_m[wave][dq] = st.m;
-      s_l[wave][dq] = L;
+      sm.m[wave][dq] = st.m;
+      sm.l[wave][dq] = L;
     }
   }
-  if (lane == 0) s_bad[wave] = bad ? 1 : 0;
+  if (lane == 0) sm.bad[wave] = bad ? 1 : 0;
   __syncthreads();
+}
 
-  // Merge the wavefronts; write this split's partial result, or (one split)
-  // the normalized output row and its LSE.
-  bool anybad = false;
+// Combines the wavefronts' results in sm into element (h, d): running max M
+// (log2 units), sum L and unnormalized o; `bad` if any wavefront met a bad
+// page.
+template <int D, int G, int NW>
+__device__ __forceinline__ void combine_waves(const PieceSmem<D, G, NW>& sm, int h, int d, float& M, float& L,
+                                              float& o) {
+  M = sm.m[0][h];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) anybad |= s_bad[w] != 0;
-  const float qnan = __builtin_nanf("");
-  const int64_t slot = ((int64_t)(b * p.num_kv_heads + g) * p.n_splits + split) * G;
-  const int64_t row0 = (int64_t)b * p.num_q_heads + g * G;  // first output row of this group
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int h = i / D, d = i % D;
-    float M = s_m[0][h];
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, sm.m[w][h]);
+  o = 0.f;
+  L = 0.f;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) o += s_acc[w][h][d] * fast_exp2(s_m[w][h] - M);
-    if constexpr (DIRECT) {
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) L += s_l[w][h] * fast_exp2(s_m[w][h] - M);
-      const float v = anybad ? qnan : o * (1.0f / L);
-      if (p.out_f32) static_cast<float*>(p.out)[(row0 + h) * D + d] = v;
-      else static_cast<f16*>(p.out)[(row0 + h) * D + d] = (f16)v;
-      if (p.lse && d == 0) p.lse[row0 + h] = anybad ? qnan : (M + log2f(L)) * kLn2;
-    } else {
-      p.part_acc[(slot + h) * D + d] = anybad ? qnan : o;
-    }
-  }
-  if (!DIRECT && threadIdx.x < G) {
-    const int h = threadIdx.x;
-    float M = s_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) L += s_l[w][h] * fast_exp2(s_m[w][h] - M);
-    p.part_ml[(slot + h) * 2 + 0] = anybad ? qnan : M;
-    p.part_ml[(slot + h) * 2 + 1] = anybad ? qnan : L;
+  for (int w = 0; w < NW; ++w) {
+    const float f = fast_exp2(sm.m[w][h] - M);
+    o += sm.acc[w][h][d] * f;
+    L += sm.l[w][h] * f;
   }
 }
 
-// One wavefront per (query head, sequence): combine the splits.
-template <int D>
+template <int D, int G, int NW>
+__device__ __forceinline__ bool any_bad(const PieceSmem<D, G, NW>& sm) {
+  bool bad = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) bad |= sm.bad[w] != 0;
+  return bad;
+}
+
+// Normalized output rows (and LSE) of the G query heads of KV head g in
+// sequence b from a piece that covers the whole sequence.
+template <int D, int G, int NW>
+__device__ __forceinline__ void write_rows(const DecodeParams& p, const PieceSmem<D, G, NW>& sm, int b, int g) {
+  const bool bad = any_bad(sm);
+  const float qnan = __builtin_nanf("");
+  const int64_t row0 = (int64_t)b * p.num_q_heads + g * G;
+  for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
+    const int h = i / D, d = i % D;
+    float M, L, o;
+    combine_waves<D, G, NW>(sm, h, d, M, L, o);
+    const float v = bad ? qnan : o * (1.0f / L);
+    if (p.out_f32) static_cast<float*>(p.out)[(row0 + h) * D + d] = v;
+    else static_cast<f16*>(p.out)[(row0 + h) * D + d] = (f16)v;
+    if (p.lse && d == 0) p.lse[row0 + h] = bad ? qnan : (M + log2f(L)) * kLn2;
+  }
+}
+
+// Partial result (unnormalized acc, max, sum) of a piece into slot `slot`
+// (G records of D + 2 floats: part_acc[slot][G][D], part_ml[slot][G][2]).
+template <int D, int G, int NW>
+__device__ __forceinline__ void write_partial(const DecodeParams& p, const PieceSmem<D, G, NW>& sm, int64_t slot) {
+  const bool bad = any_bad(sm);
+  const float qnan = __builtin_nanf("");
+  for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
+    const int h = i / D, d = i % D;
+    float M, L, o;
+    combine_waves<D, G, NW>(sm, h, d, M, L, o);
+    p.part_acc[(slot * G + h) * D + d] = bad ? qnan : o;
+    if (d == 0) {
+      p.part_ml[(slot * G + h) * 2 + 0] = bad ? qnan : M;
+      p.part_ml[(slot * G + h) * 2 + 1] = bad ? qnan : L;
+    }
+  }
+}
+
+// NW wavefronts per workgroup = (split, KV head g, sequence b).  DIRECT (one
+// split per sequence, p.n_splits == 1): the workgroup normalizes its result
+// and writes out / lse itself, and no merge kernel runs.
+template <int D, int G, int MODE, int NW, bool DIRECT>
+__global__ __launch_bounds__(NW * kWave, kMinWaves) void decode_splitk_kernel(DecodeParams p) {
+  __shared__ PieceSmem<D, G, NW> sm;
+  const int lane = threadIdx.x & (kWave - 1);
+  // wavefront index made provably uniform, so page metadata becomes scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int split = kHeadMajorGrid ? blockIdx.y : blockIdx.x;
+  const int g = kHeadMajorGrid ? blockIdx.x : blockIdx.y;
+  const int b = blockIdx.z;
+  const int len = min(max(p.seq_lens[b], 0), p.max_seq_len);
+  const int npages = (len + kPage - 1) / kPage;
+  const int pbeg = split * p.pages_per_split;
+  if (pbeg >= npages) {  // the merge ignores splits past the sequence end
+    if (DIRECT) write_empty_rows<D, G>(p, b, g);  // len 0: out 0, lse -inf
+    return;
+  }
+  const int pend = min(pbeg + p.pages_per_split, npages);
+  run_piece<D, G, MODE, NW>(p, sm, b, g, len, pbeg, pend, lane, wave);
+  if constexpr (DIRECT) write_rows<D, G, NW>(p, sm, b, g);
+  else write_partial<D, G, NW>(p, sm, ((int64_t)(b * p.num_kv_heads + g) * p.n_splits + split));
+}
+
+// ---------------------------------------------------------------------------
+// Balanced plan for ragged batches.  All page-heads of the batch, in the
+// order (sequence, KV head, page), are cut into n_wg equal ranges
+// [r(i), r(i+1)), r(i) = floor(i W / n_wg), one per workgroup, in one round.
+// A workgroup walks its range piece by piece (a piece = the part of one
+// (sequence, KV head) inside the range): a piece that is a whole (sequence,
+// KV head) is written as output directly; a piece cut by the range ends is a
+// partial result in the workgroup's slot 0 (the piece at the start of the
+// range) or slot 1 (the piece at its end).  The merge kernel then combines,
+// for each cut (sequence, KV head), the tail piece of its first workgroup and
+// the head pieces of the following ones.
+
+__device__ __forceinline__ int seq_pages(const DecodeParams& p, int b) {
+  return (min(max(p.seq_lens[b], 0), p.max_seq_len) + kPage - 1) / kPage;
+}
+
+// Workgroup whose range holds flattened position x.
+__device__ __forceinline__ int wg_of(int64_t x, int64_t W, int n) { return (int)(((x + 1) * n - 1) / W); }
+__device__ __forceinline__ int64_t wg_start(int i, int64_t W, int n) { return (int64_t)i * W / n; }
+
+template <int D, int G, int MODE>
+__global__ __launch_bounds__(4 * kWave, 2) void decode_balanced_kernel(DecodeParams p) {
+  constexpr int NW = 4;
+  __shared__ PieceSmem<D, G, NW> sm;
+  __shared__ int s_pref[kDecodeMaxBalancedBatch + 1];  // exclusive prefix sums of page counts
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int B = p.batch;
+  if (wave == 0) {  // one wavefront scans the page counts
+    const int per = (B + kWave - 1) / kWave;
+    const int lo = lane * per, hi = min(B, lo + per);
+    int sum = 0;
+    for (int b = lo; b < hi; ++b) sum += seq_pages(p, b);
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += t;
+    }
+    int run = incl - sum;
+    for (int b = lo; b < hi; ++b) {
+      s_pref[b] = run;
+      run += seq_pages(p, b);
+    }
+    if (lane == kWave - 1) s_pref[B] = incl;
+  }
+  __syncthreads();
+  const int H = p.num_kv_heads;
+  const int64_t W = (int64_t)H * s_pref[B];
+  const int n = p.n_wg, i = blockIdx.x;
+  const int64_t w0 = wg_start(i, W, n), w1 = wg_start(i + 1, W, n);
+  if (w0 == w1) {  // empty range (fewer page-heads than workgroups): a neutral head record,
+    // since the merge reads the head slots of every workgroup a cut sequence spans
+    for (int e = threadIdx.x; e < G * D; e += 4 * kWave) {
+      p.part_acc[2 * (int64_t)i * G * D + e] = 0.f;
+      if (e < G) {
+        p.part_ml[(2 * (int64_t)i * G + e) * 2 + 0] = kNegBig;
+        p.part_ml[(2 * (int64_t)i * G + e) * 2 + 1] = 0.f;
+      }
+    }
+    return;
+  }
+  int64_t q = w0;
+  while (q < w1) {
+    // sequence of position q: the last b with H * pref[b] <= q (skips empty ones)
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)H * s_pref[mid] <= q) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = lo;
+    const int np = s_pref[b + 1] - s_pref[b];
+    const int64_t off = q - (int64_t)H * s_pref[b];
+    const int g = (int)(off / np);
+    const int page = (int)(off - (int64_t)g * np);
+    const int64_t seg = (int64_t)H * s_pref[b] + (int64_t)g * np;
+    const int pend = (int)(min(w1, seg + np) - seg);
+    const int len = min(max(p.seq_lens[b], 0), p.max_seq_len);
+    run_piece<D, G, MODE, NW>(p, sm, b, g, len, page, pend, lane, wave);
+    if (page == 0 && pend == np) write_rows<D, G, NW>(p, sm, b, g);
+    else write_partial<D, G, NW>(p, sm, 2 * (int64_t)i + (q == w0 ? 0 : 1));
+    q = seg + pend;
+    __syncthreads();  // sm is reused by the next piece
+  }
+}
+
+// One wavefront per (query head, sequence): combine the partial results.
+// Split plan: splits 0 .. nsplit-1 of the sequence.  Balanced plan: the
+// pieces of the workgroups whose ranges cut this (sequence, KV head); a
+// (sequence, KV head) inside one range was written by its workgroup.
+template <int D, bool BALANCED>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeParams p) {
   constexpr int PER = D / kWave;
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
@@ -514,8 +646,42 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeParams p) {
   const int g = h / G, hh = h - g * G;
   const int len = min(max(p.seq_lens[b], 0), p.max_seq_len);
   const int npages = (len + kPage - 1) / kPage;
-  const int nsplit = (npages + p.pages_per_split - 1) / p.pages_per_split;
   const int64_t row = (int64_t)b * p.num_q_heads + h;
+
+  int nsplit;
+  int64_t slot0 = 0, first = 0;  // record of piece s: s == 0 ? first : slot0 + 2 s
+  if constexpr (BALANCED) {
+    int before = 0, total = 0;
+    for (int x = lane; x < p.batch; x += kWave) {
+      const int n = seq_pages(p, x);
+      total += n;
+      before += x < b ? n : 0;
+    }
+#pragma unroll
+    for (int x = 1; x < kWave; x <<= 1) {
+      total += __shfl_xor(total, x, kWave);
+      before += __shfl_xor(before, x, kWave);
+    }
+    if (npages == 0) {
+      nsplit = 0;
+    } else {
+      const int64_t W = (int64_t)p.num_kv_heads * total;
+      const int64_t start = (int64_t)p.num_kv_heads * before + (int64_t)g * npages;
+      const int i0 = wg_of(start, W, p.n_wg), i1 = wg_of(start + npages - 1, W, p.n_wg);
+      if (i0 == i1) return;  // written by its workgroup
+      nsplit = i1 - i0 + 1;
+      first = 2 * (int64_t)i0 + (start == wg_start(i0, W, p.n_wg) ? 0 : 1);
+      slot0 = 2 * (int64_t)i0;  // piece s >= 1: head slot of workgroup i0 + s
+    }
+  } else {
+    nsplit = (npages + p.pages_per_split - 1) / p.pages_per_split;
+    first = (int64_t)(b * p.num_kv_heads + g) * p.n_splits;
+    slot0 = first;
+  }
+  auto rec = [&](int s) -> int64_t {
+    const int64_t slot = BALANCED ? (s == 0 ? first : slot0 + 2 * (int64_t)s) : slot0 + s;
+    return slot * G + hh;
+  };
 
   float o[PER];
   float lse_v;
@@ -524,14 +690,13 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeParams p) {
     for (int i = 0; i < PER; ++i) o[i] = 0.f;
     lse_v = -__builtin_inff();
   } else {
-    const int64_t base = (int64_t)(b * p.num_kv_heads + g) * p.n_splits;
     // split statistics are spread over the lanes (split s in lane s % 64), so
     // their loads and the max / sum reductions run in parallel
     float M = kNegBig;
     bool bad = false;
     for (int s0 = 0; s0 < nsplit; s0 += kWave) {
       const int s = s0 + lane;
-      const float ms = s < nsplit ? p.part_ml[((base + s) * G + hh) * 2] : kNegBig;
+      const float ms = s < nsplit ? p.part_ml[rec(s) * 2] : kNegBig;
       bad |= ms != ms;
       M = fmaxf(M, ms);
     }
@@ -545,7 +710,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeParams p) {
       const int s = s0 + lane;
       float f_lane = 0.f;
       if (s < nsplit) {
-        const int64_t k = (base + s) * G + hh;
+        const int64_t k = rec(s);
         f_lane = fast_exp2(p.part_ml[k * 2] - M);
         L += p.part_ml[k * 2 + 1] * f_lane;
       }
@@ -553,7 +718,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll 4
       for (int j = 0; j < cnt; ++j) {
         const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f_lane), j));
-        const int64_t k = (base + s0 + j) * G + hh;
+        const int64_t k = rec(s0 + j);
 #pragma unroll
         for (int i = 0; i < PER; ++i) o[i] += p.part_acc[k * D + lane + kWave * i] * f;
       }
@@ -597,7 +762,24 @@ hipError_t launch_split(const DecodeParams& p, dim3 grid, hipStream_t stream) {
 }
 
 template <int D, int G>
+hipError_t launch_balanced(const DecodeParams& p, hipStream_t stream) {
+  const int mode = p.has_base ? (p.fidelity ? 2 : 3) : (p.fidelity ? 1 : 0);
+  const dim3 grid(p.n_wg), block(4 * kWave);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL((decode_balanced_kernel<D, G, 0>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((decode_balanced_kernel<D, G, 1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_balanced_kernel<D, G, 2>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((decode_balanced_kernel<D, G, 3>), grid, block, 0, stream, p); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D, true>), dim3(p.num_q_heads, p.batch), dim3(kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, int G>
 hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
+  if (p.n_wg > 0) return launch_balanced<D, G>(p, stream);
   const dim3 grid = kHeadMajorGrid ? dim3(p.num_kv_heads, p.n_splits, p.batch)
                                    : dim3(p.n_splits, p.num_kv_heads, p.batch);
   if (p.n_splits == 1) {
@@ -610,7 +792,7 @@ hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
     const hipError_t e = launch_split<D, G, 4, false>(p, grid, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(p.num_q_heads, p.batch), dim3(kWave), 0, stream,
+  hipLaunchKernelGGL((decode_merge_kernel<D, false>), dim3(p.num_q_heads, p.batch), dim3(kWave), 0, stream,
                      p);
   return hipGetLastError();
 }
@@ -651,6 +833,23 @@ size_t decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_h
   const size_t acc = rows * head_dim * sizeof(float);
   const size_t acc_aligned = (acc + 255) & ~(size_t)255;
   return acc_aligned + rows * 2 * sizeof(float);
+}
+
+int32_t decode_balanced_workgroups(int32_t batch, int32_t num_kv_heads, int32_t max_pages) {
+  // one round: 2 four-wavefront workgroups per CU on the 256-CU part (the
+  // kernel holds 2 wavefronts per SIMD), more (whole rounds) when a range
+  // would exceed the LDS page-metadata stage
+  const int64_t work = (int64_t)batch * num_kv_heads * max_pages;
+  int64_t n = kBalancedRound;
+  while ((work + n - 1) / n > kMaxSplitPages) n += kBalancedRound;
+  return (int32_t)n;
+}
+
+size_t decode_balanced_scratch_bytes(int32_t n_wg, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim) {
+  const size_t recs = (size_t)n_wg * 2 * (num_q_heads / num_kv_heads);
+  const size_t acc = (recs * head_dim * sizeof(float) + 255) & ~(size_t)255;
+  return acc + recs * 2 * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {

@@ -103,8 +103,9 @@ int32_t ekv_decode_plan_pages_per_split(const int32_t* seq_lens_host, int32_t ba
   if (maxp == 0) return 16;
   if (total * 10 >= maxp * batch * 9)  // lengths within ~10% of the longest: one balanced round
     return ekv::decode_auto_pages_per_split(batch, num_kv_heads, (int32_t)maxp);
-  // ragged lengths: small splits (about 4096 of them over all KV heads) balance the tail
-  int64_t c = (total * num_kv_heads + 4095) / 4096;
+  // ragged lengths: equal shares of all page-heads per workgroup
+  if (batch <= ekv::kDecodeMaxBalancedBatch) return EKV_DECODE_BALANCED;
+  int64_t c = (total * num_kv_heads + 4095) / 4096;  // else small splits balance the tail
   c = (c + 3) / 4 * 4;
   return (int32_t)(c < 16 ? 16 : (c > 512 ? 512 : c));
 }
@@ -112,6 +113,11 @@ int32_t ekv_decode_plan_pages_per_split(const int32_t* seq_lens_host, int32_t ba
 size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_seq_len, int32_t pages_per_split) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
+  if (pages_per_split == EKV_DECODE_BALANCED) {
+    if (num_q_heads % num_kv_heads != 0) return 0;
+    const int32_t n = ekv::decode_balanced_workgroups(batch, num_kv_heads, ceil_div(max_seq_len, EKV_PAGE_SIZE));
+    return ekv::decode_balanced_scratch_bytes(n, num_q_heads, num_kv_heads, head_dim);
+  }
   const int32_t pps = pages_per_split > 0 ? pages_per_split
                                           : ekv_decode_pages_per_split(batch, num_kv_heads, max_seq_len);
   const int32_t splits = ceil_div(ceil_div(max_seq_len, EKV_PAGE_SIZE), pps);
@@ -153,11 +159,18 @@ ekv_status decode_impl(const ekv_paged_kv* kv, const void* q, int32_t batch, int
     if (has_t == has_c) return fail(EKV_ERR_INVALID_ARG, "fidelity may be NULL only when exactly one pool is non-empty");
     uniform_kind = has_c ? EKV_FIDELITY_COMPACT : EKV_FIDELITY_TARGET;
   }
-  if (pages_per_split < 0 || pages_per_split > 512) return fail(EKV_ERR_INVALID_ARG, "pages_per_split %d outside 0..512", pages_per_split);
-  const int32_t pps = pages_per_split > 0 ? pages_per_split
-                                          : ekv_decode_pages_per_split(batch, kv->num_kv_heads, max_seq_len);
-  const int32_t splits = max_pages > 0 ? ceil_div(max_pages, pps) : 0;
-  const size_t need = ekv::decode_scratch_bytes(batch, num_q_heads, kv->num_kv_heads, kv->head_dim, splits);
+  const bool balanced = pages_per_split == EKV_DECODE_BALANCED;
+  if (!balanced && (pages_per_split < 0 || pages_per_split > 512))
+    return fail(EKV_ERR_INVALID_ARG, "pages_per_split %d outside 0..512 and not EKV_DECODE_BALANCED", pages_per_split);
+  if (balanced && batch > ekv::kDecodeMaxBalancedBatch)
+    return fail(EKV_ERR_UNSUPPORTED, "balanced plan takes at most %d sequences", ekv::kDecodeMaxBalancedBatch);
+  const int32_t pps = balanced ? 0
+                      : pages_per_split > 0 ? pages_per_split
+                                            : ekv_decode_pages_per_split(batch, kv->num_kv_heads, max_seq_len);
+  const int32_t splits = balanced ? 0 : max_pages > 0 ? ceil_div(max_pages, pps) : 0;
+  const int32_t n_wg = balanced ? ekv::decode_balanced_workgroups(batch, kv->num_kv_heads, max_pages) : 0;
+  const size_t need = balanced ? ekv::decode_balanced_scratch_bytes(n_wg, num_q_heads, kv->num_kv_heads, kv->head_dim)
+                               : ekv::decode_scratch_bytes(batch, num_q_heads, kv->num_kv_heads, kv->head_dim, splits);
   if (need > 0) {  // more than one split: partial results go through scratch
     if (!scratch) return fail(EKV_ERR_INVALID_ARG, "scratch is NULL (%zu bytes needed)", need);
     if (((uintptr_t)scratch & 255u) != 0) return fail(EKV_ERR_INVALID_ARG, "scratch not 256-byte aligned");
@@ -189,8 +202,10 @@ ekv_status decode_impl(const ekv_paged_kv* kv, const void* q, int32_t batch, int
   p.max_seq_len = max_seq_len;
   p.pages_per_split = pps;
   p.n_splits = splits;
+  p.n_wg = max_pages > 0 ? n_wg : 0;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  const size_t rows = (size_t)batch * num_q_heads * (size_t)splits;
+  const size_t rows = balanced ? (size_t)n_wg * 2 * (num_q_heads / kv->num_kv_heads)
+                               : (size_t)batch * num_q_heads * (size_t)splits;
   p.part_acc = need > 0 ? static_cast<float*>(scratch) : nullptr;
   p.part_ml = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(scratch) +
                                                     ((rows * kv->head_dim * sizeof(float) + 255) & ~(size_t)255))

@@ -25,9 +25,10 @@ struct DecodeParams {
   const int32_t* seq_lens;
   int32_t batch, num_q_heads, num_kv_heads, head_dim, max_seq_len;
   int32_t pages_per_split, n_splits;
+  int32_t n_wg;      // balanced plan: workgroups sharing all page-heads equally (0: split plan)
   float scale_log2;  // sm_scale * log2(e)
-  float* part_acc;   // [batch][Hkv][n_splits][G][D]
-  float* part_ml;    // [batch][Hkv][n_splits][G][2]  (max in log2 units, sum)
+  float* part_acc;   // split plan [batch][Hkv][n_splits][G][D]; balanced [n_wg][2][G][D]
+  float* part_ml;    // the same records' (max in log2 units, sum)
   void* out;
   int32_t out_f32;
   float* lse;
@@ -117,6 +118,12 @@ struct PackParams {
 int32_t decode_auto_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages);
 size_t decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t n_splits);
+// Balanced plan: workgroups for a batch whose longest sequence has max_pages
+// pages, and the scratch bytes of their partial results.
+constexpr int32_t kDecodeMaxBalancedBatch = 2048;
+int32_t decode_balanced_workgroups(int32_t batch, int32_t num_kv_heads, int32_t max_pages);
+size_t decode_balanced_scratch_bytes(int32_t n_wg, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim);
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);

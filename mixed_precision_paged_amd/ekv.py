@@ -24,6 +24,7 @@ FIDELITY_TARGET = 0
 FIDELITY_COMPACT = 1
 FIDELITY_BASE = 2
 MAX_PREFILL_TOKENS = 8192
+DECODE_BALANCED = -1  # pages_per_split: equal shares of all page-heads per workgroup
 
 EKV_OK = 0
 EKV_ERR_INVALID_ARG = 1

@@ -93,6 +93,14 @@ def test_split_plan_and_scratch_size():
     assert ekv.ekv_decode_pages_per_split(16, 8, 8192) == 128
     # 512 groups: one split each
     assert ekv.ekv_decode_pages_per_split(64, 8, 8192) == 512
+    # balanced plan: 512 workgroups (2 per CU) x 2 partial records of G x (D + 2) floats
+    bal = ekv.ekv_decode_scratch_bytes(64, 32, 8, 128, 8192, ekv.DECODE_BALANCED)
+    recs = 512 * 2 * 4
+    assert bal == ((recs * 128 * 4 + 255) // 256) * 256 + recs * 2 * 4
+    # whole rounds more once a share could pass 512 pages: 64 x 8 x 2048 pages -> 2048
+    recs = 2048 * 2 * 4
+    assert ekv.ekv_decode_scratch_bytes(64, 32, 8, 128, 32768, ekv.DECODE_BALANCED) == \
+        ((recs * 128 * 4 + 255) // 256) * 256 + recs * 2 * 4
     assert ekv.ekv_decode_scratch_bytes(2, 4, 1, 64, 64, 1) == ((2 * 4 * 4 * 64 * 4 + 255) // 256) * 256 + 2 * 4 * 4 * 8
     assert ekv.ekv_decode_scratch_bytes(0, 4, 1, 64, 64, 1) == 0
 
@@ -102,8 +110,11 @@ def test_split_plan_from_host_lengths():
     uniform = ekv.ekv_decode_plan_pages_per_split(np.full(32, 8192), 8)
     assert uniform == ekv.ekv_decode_pages_per_split(32, 8, 8192) == 512
     lens = np.random.default_rng(0).integers(1024, 16385, size=64)
-    ragged = ekv.ekv_decode_plan_pages_per_split(lens, 8)
-    pages = int(((lens + 15) // 16).sum())
+    assert ekv.ekv_decode_plan_pages_per_split(lens, 8) == ekv.DECODE_BALANCED
+    # beyond the balanced plan's batch limit: small splits
+    big = np.random.default_rng(0).integers(64, 1025, size=2049)
+    ragged = ekv.ekv_decode_plan_pages_per_split(big, 8)
+    pages = int(((big + 15) // 16).sum())
     assert ragged % 4 == 0 and 16 <= ragged <= 512 and abs(ragged - pages * 8 / 4096) <= 4
     assert ekv.ekv_decode_plan_pages_per_split([], 8) == 16
     assert ekv.ekv_decode_plan_pages_per_split([0, 0], 8) == 16

@@ -88,9 +88,11 @@ def test_split_plans_agree():
     e = synth.make_elastic_case(80, [3000, 2100, 700], 8, 2, 128, sink_pages=2, recent_pages=6)
     c = e.paged
     want, _ = _oracle(c)
-    for pps in (16, 64, 512):
+    for pps in (16, 64, 512, ekv().DECODE_BALANCED):
         out, _ = _elastic_decode(c, structured_bounds=e.base_bounds, flags=False, pps=pps)
         assert_close(out, want, what=f"pages_per_split {pps}")
+        out, _ = _elastic_decode(c, pps=pps)  # general path (flag table)
+        assert_close(out, want, what=f"flags, pages_per_split {pps}")
 
 
 def test_base_flags_without_indicator_are_invalid():

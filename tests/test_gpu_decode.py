@@ -57,13 +57,47 @@ def test_split_count_does_not_change_the_result():
     dc = DeviceCase(c)
     want, wlse = oracle_decode(c)
     outs = []
-    for pps in (1, 3, 16, 64, 0, 512):
+    for pps in (1, 3, 16, 64, 0, 512, ekv().DECODE_BALANCED):
         out, lse = dc.decode(torch.float32, pages_per_split=pps)
         assert_close(out, want, what=f"pages_per_split={pps}")
         assert_lse_close(lse, wlse)
         outs.append(out)
     for o in outs[1:]:
         assert max_abs(o, outs[0]) <= TOL
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 2, 64)])
+def test_balanced_plan_ragged_empty_and_bad(hq, hkv, d):
+    """Equal page-head shares per workgroup: sequences held whole by one range (1-page
+    ones), cut over a few ranges and spread over hundreds (few page-heads, 512
+    workgroups), empty ones, and a bad page id that must turn only its rows NaN."""
+    step(f"decode balanced plan hq={hq} hkv={hkv} d={d}")
+    lens = [1, 5, 16, 0, 17, 300, 2053, 40, 0, 1000, 3, 129, 64, 16, 777, 2]
+    c = synth.make_paged_case(300 + d, lens, hq, hkv, d, compact_frac=0.4,
+                              outlier_frac=0.01, outlier_mult=20.0)
+    dc = DeviceCase(c)
+    want, wlse = oracle_decode(c)
+    out, lse = dc.decode(torch.float32, pages_per_split=ekv().DECODE_BALANCED)
+    assert_close(out, want)
+    assert_lse_close(lse, wlse)
+    empty = np.array(lens) == 0
+    assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    out16, _ = dc.decode(torch.float16, pages_per_split=ekv().DECODE_BALANCED)
+    assert f16_bits_equal_rne(out16, out)
+    # a short batch: 37 + 1 tokens spread over 512 workgroups
+    c2 = synth.make_paged_case(310 + d, [37, 1], hq, hkv, d, compact_frac=0.5)
+    out2, lse2 = DeviceCase(c2).decode(torch.float32, pages_per_split=ekv().DECODE_BALANCED)
+    w2, wl2 = oracle_decode(c2)
+    assert_close(out2, w2)
+    assert_lse_close(lse2, wl2)
+    # one bad page id in sequence 6 (2053 tokens, cut over several ranges)
+    bad = c.page_table.copy()
+    bad[6, 70] = 1 << 20
+    dc.page_table = dev(bad)
+    outb, lseb = dc.decode(torch.float32, pages_per_split=ekv().DECODE_BALANCED)
+    assert np.all(np.isnan(outb[6])) and np.all(np.isnan(lseb[6]))
+    keep = [i for i in range(len(lens)) if i != 6]
+    assert_close(outb[keep], want[keep])
 
 
 def test_page_permutation_gives_identical_output():

@@ -44,7 +44,9 @@ constexpr float kTau = 8.0f;          // deferred-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;   // "no token yet" running max
 constexpr bool kHeadMajorGrid = true; // launch order: the KV heads of one (sequence, split) adjacent
 constexpr int kMaxSplitPages = 512;   // pages per split (metadata staged in LDS)
-constexpr int kBalancedRound = 512;   // balanced plan: workgroups per round
+constexpr int kBalancedRound = 512;     // balanced plan: workgroups per round (2 per CU)
+constexpr int kBalancedMaxPages = 512;  // balanced plan: pages per range (LDS stage); measured
+                                        // better than one round of up to 1,024-page ranges
 constexpr int kSlots = 2;             // register page buffers per wavefront (pages in flight + 1)
 constexpr int kMinWaves = 2;          // occupancy bound (wavefronts per SIMD) for G*D < 1024
 
@@ -295,13 +297,14 @@ __device__ void write_empty_rows(const DecodeParams& p, int b, int g) {
 }
 
 // LDS of one workgroup of NW wavefronts working on one piece of a sequence.
-template <int D, int G, int NW>
+template <int D, int G, int NW, int MAXP = kMaxSplitPages>
 struct PieceSmem {
+  static constexpr int kMaxPages = MAXP;
   float acc[NW][G][D];
   float m[NW][G];
   float l[NW][G];
   int bad[NW];
-  int meta[kMaxSplitPages];
+  int meta[MAXP];
 };
 
 // MODE 0: every page has kind p.uniform_kind (no flag table); 1: per-page flags
@@ -311,12 +314,12 @@ struct PieceSmem {
 // others TARGET, with no flag table.
 //
 // Attention of the G query heads of KV head g of sequence b (length len) over
-// its logical pages [pbeg, pend) (at most kMaxSplitPages): the NW wavefronts
+// its logical pages [pbeg, pend) (at most SM::kMaxPages): the NW wavefronts
 // take the pages round-robin and leave their (max, sum, unnormalized acc) and
 // bad-page flags in sm, published by a barrier.  The caller must not reuse sm
 // before every wavefront has read what it needs (a barrier).
-template <int D, int G, int MODE, int NW>
-__device__ __forceinline__ void run_piece(const DecodeParams& p, PieceSmem<D, G, NW>& sm, int b, int g, int len,
+template <int D, int G, int MODE, int NW, class SM>
+__device__ __forceinline__ void run_piece(const DecodeParams& p, SM& sm, int b, int g, int len,
                                           int pbeg, int pend, int lane, int wave) {
   constexpr int kThreads = NW * kWave;
   constexpr int kWaves = NW;
@@ -462,8 +465,8 @@ __device__ __forceinline__ void run_piece(const DecodeParams& p, PieceSmem<D, G,
 // Combines the wavefronts' results in sm into element (h, d): running max M
 // (log2 units), sum L and unnormalized o; `bad` if any wavefront met a bad
 // page.
-template <int D, int G, int NW>
-__device__ __forceinline__ void combine_waves(const PieceSmem<D, G, NW>& sm, int h, int d, float& M, float& L,
+template <int D, int G, int NW, class SM>
+__device__ __forceinline__ void combine_waves(const SM& sm, int h, int d, float& M, float& L,
                                               float& o) {
   M = sm.m[0][h];
 #pragma unroll
@@ -478,8 +481,8 @@ __device__ __forceinline__ void combine_waves(const PieceSmem<D, G, NW>& sm, int
   }
 }
 
-template <int D, int G, int NW>
-__device__ __forceinline__ bool any_bad(const PieceSmem<D, G, NW>& sm) {
+template <int NW, class SM>
+__device__ __forceinline__ bool any_bad(const SM& sm) {
   bool bad = false;
 #pragma unroll
   for (int w = 0; w < NW; ++w) bad |= sm.bad[w] != 0;
@@ -488,9 +491,9 @@ __device__ __forceinline__ bool any_bad(const PieceSmem<D, G, NW>& sm) {
 
 // Normalized output rows (and LSE) of the G query heads of KV head g in
 // sequence b from a piece that covers the whole sequence.
-template <int D, int G, int NW>
-__device__ __forceinline__ void write_rows(const DecodeParams& p, const PieceSmem<D, G, NW>& sm, int b, int g) {
-  const bool bad = any_bad(sm);
+template <int D, int G, int NW, class SM>
+__device__ __forceinline__ void write_rows(const DecodeParams& p, const SM& sm, int b, int g) {
+  const bool bad = any_bad<NW>(sm);
   const float qnan = __builtin_nanf("");
   const int64_t row0 = (int64_t)b * p.num_q_heads + g * G;
   for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
@@ -506,9 +509,9 @@ __device__ __forceinline__ void write_rows(const DecodeParams& p, const PieceSme
 
 // Partial result (unnormalized acc, max, sum) of a piece into slot `slot`
 // (G records of D + 2 floats: part_acc[slot][G][D], part_ml[slot][G][2]).
-template <int D, int G, int NW>
-__device__ __forceinline__ void write_partial(const DecodeParams& p, const PieceSmem<D, G, NW>& sm, int64_t slot) {
-  const bool bad = any_bad(sm);
+template <int D, int G, int NW, class SM>
+__device__ __forceinline__ void write_partial(const DecodeParams& p, const SM& sm, int64_t slot) {
+  const bool bad = any_bad<NW>(sm);
   const float qnan = __builtin_nanf("");
   for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
     const int h = i / D, d = i % D;
@@ -570,7 +573,7 @@ __device__ __forceinline__ int64_t wg_start(int i, int64_t W, int n) { return (i
 template <int D, int G, int MODE>
 __global__ __launch_bounds__(4 * kWave, 2) void decode_balanced_kernel(DecodeParams p) {
   constexpr int NW = 4;
-  __shared__ PieceSmem<D, G, NW> sm;
+  __shared__ PieceSmem<D, G, NW, kBalancedMaxPages> sm;
   __shared__ int s_pref[kDecodeMaxBalancedBatch + 1];  // exclusive prefix sums of page counts
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -841,7 +844,7 @@ int32_t decode_balanced_workgroups(int32_t batch, int32_t num_kv_heads, int32_t 
   // would exceed the LDS page-metadata stage
   const int64_t work = (int64_t)batch * num_kv_heads * max_pages;
   int64_t n = kBalancedRound;
-  while ((work + n - 1) / n > kMaxSplitPages) n += kBalancedRound;
+  while ((work + n - 1) / n > kBalancedMaxPages) n += kBalancedRound;
   return (int32_t)n;
 }
 

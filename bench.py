@@ -127,24 +127,25 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, events on the launch stream around each decode call
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region: K back-to-back steps between two events on the launch stream;
+    # the average launch duration is the region's event time / K (events between
+    # the calls would add their own dispatch gaps to every call)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        evs[i][0].record(stream)
         step(i)
-        evs[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    per_call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    region_ms = ev0.elapsed_time(ev1)
 
     algo_bytes = bytemodel.decode_bytes(case.seq_lens, case.fidelity, Hq, Hkv, D, out_bytes=2,
                                         lse=False, flags_read=fl is not None)
     ms_per_step = wall * 1e3 / args.steps
     value = algo_bytes / (ms_per_step * 1e-3) / 1e9
-    kernel_ms = float(per_call_ms.mean())
+    kernel_ms = region_ms / args.steps
     achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
     single_split = -(-int(case.max_seq_len) // 16) <= pps
 
@@ -398,17 +399,17 @@ def bench_writer(args):
     k_step, v_step = kr[:32].contiguous(), vr[:32].contiguous()
     stream = torch.cuda.current_stream()
 
-    def timed(fn, steps):
+    def timed(fn, steps):  # seconds per call: back-to-back calls between two events
         for _ in range(max(1, args.warmup)):
             fn()
         torch.cuda.synchronize()
-        evs = _events(steps)
-        for a, b in evs:
-            a.record(stream)
+        (a, b), = _events(1)
+        a.record(stream)
+        for _ in range(steps):
             fn()
-            b.record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+        return a.elapsed_time(b) * 1e-3 / steps
 
     steps = max(1, min(args.steps, 20))
     tq = timed(lambda: ekv.ekv_quantize_pages(kv, kr, vr, rs, dst, nv, stream=stream), steps)
@@ -485,17 +486,17 @@ def bench_elastic(args):
     kv_t = ekv.paged_kv(Hkv, D, dev(t.k_target), dev(t.v_target))
     pt_t, lens_t = dev(t.page_table), dev(t.seq_lens)
 
-    def timed(fn, steps):
+    def timed(fn, steps):  # seconds per call: back-to-back calls between two events
         for _ in range(max(1, args.warmup)):
             fn()
         torch.cuda.synchronize()
-        evs = _events(steps)
-        for a, b in evs:
-            a.record(stream)
+        (a, b), = _events(1)
+        a.record(stream)
+        for _ in range(steps):
             fn()
-            b.record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+        return a.elapsed_time(b) * 1e-3 / steps
 
     steps = max(1, min(args.steps, 50))
     for _ in range(10):  # clocks and caches up before any variant is timed

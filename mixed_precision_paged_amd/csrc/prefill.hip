@@ -338,6 +338,12 @@ __device__ __forceinline__ void load_v_paged(VRegs& r, PagedSrc src, const TileM
   }
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l writes bytes
+// [16 l, 16 l + 16) after `dst` (wave-uniform); out-of-range lanes write zeros.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, f16* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+
 // Writes NaN to output rows [r_lo, r_hi) of head h (and their LSE).
 template <int D>
 __device__ void write_nan_rows(const PrefillParams& p, int64_t q0, int r_lo, int r_hi, int h) {
@@ -356,6 +362,11 @@ template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, int n_mtiles) {
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
+  // Paged source, head dim 128: K tiles go from the pages straight into LDS
+  // (wavefront w stages page w of the tile, 4 row quads of 1 KiB), unpadded
+  // with 16-byte chunk c of row r at chunk c ^ (r % 16), as in the workspace
+  // kernel; no K staging registers.
+  constexpr bool KDMA = PAGED && D == 128;
   // K of tiles i + 1 (computing S ahead) and i + 2 (being stored), V of
   // tiles i (P.V) and i + 1 (being stored)
   __shared__ SmemK<D> kbuf[2];
@@ -508,10 +519,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   vreg.v_codes = false;
   vreg.vscale = 1.0f;
 
+  // KDMA: this lane's row quad j of its wavefront's page: row 4 j + l / 16,
+  // swizzled chunk l % 16 holds source chunk (l % 16) ^ row
+  uint32_t kdo[4] = {0u, 0u, 0u, 0u};
+  if constexpr (KDMA) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      kdo[j] = (uint32_t)r * rowb + 16u * (uint32_t)((lane & 15) ^ r);
+    }
+  }
   auto issue_k = [&](int t, const TileMetaRaw& tm) {
-    if constexpr (PAGED) load_k_paged<D>(kreg, src, tm, wave_u, pkoff);
-    else load_k<D>(kreg, kr, koff, (uint32_t)(t * kN) * rowb);
+    if constexpr (KDMA) {
+      const TileMeta um = uniform_meta(tm);
+      const PageDesc pd = page_desc(src, tm_meta(um, wave_u), tm_scale(um, wave_u));
+      f16* dst = kbuf[t & 1].k + 16 * wave_u * D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lds_dma16(pd.k, dst + 4 * j * D, kdo[j]);
+    } else if constexpr (PAGED) {
+      load_k_paged<D>(kreg, src, tm, wave_u, pkoff);
+    } else {
+      load_k<D>(kreg, kr, koff, (uint32_t)(t * kN) * rowb);
+    }
   };
+  // K tile to LDS: KDMA tiles are already there (their loads are waited for
+  // before the barrier that publishes them)
+  auto put_k = [&](SmemK<D>& sk) {
+    if constexpr (!KDMA) store_k<D>(sk, kreg);
+  };
+  // QK^T A-operand offsets (halves) of k-step ks inside a 32-row key block
+  uint32_t kro[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    kro[ks] = KDMA ? (uint32_t)col * D + 8u * (uint32_t)((2 * ks + half) ^ (col & 15))
+                   : (uint32_t)col * SmemK<D>::kStride + 8u * (uint32_t)half + 16u * (uint32_t)ks;
   auto issue_v = [&](int t, const TileMetaRaw& tm) {
     if constexpr (PAGED) load_v_paged<D>(vreg, src, tm, wave_u, lane, pvoff16, pvoff8);
     else load_v(vreg, vr, voff, (uint32_t)(t * kN) * rowb);
@@ -528,10 +569,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   // S^T = K . Q^T of one 32-key block of a tile (8 MFMAs over the head dim)
   auto qk_block = [&](f32x16& sacc, const SmemK<D>& sk, int kb) {
     sacc = f32x16{};
-    const f16* kp = &sk.k[(kb * 32 + col) * SmemK<D>::kStride + 8 * half];
+    const f16* kp = &sk.k[kb * 32 * (KDMA ? D : SmemK<D>::kStride)];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const f16x8 a = *reinterpret_cast<const f16x8*>(kp + 16 * ks);
+      const f16x8 a = *reinterpret_cast<const f16x8*>(kp + kro[ks]);
       sacc = mfma32(a, qb[ks], sacc);
     }
   };
@@ -605,20 +646,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
     }
   };
 
-  // Prologue: K(0), V(0), K(1) into LDS, then S(0).  Paged source: tile
-  // metadata is read from LDS one iteration before its loads are issued;
-  // tmk belongs to the next K tile, tmv to the next V tile.
-  TileMetaRaw tmk = meta(0), tmv{};
-  issue_k(0, tmk);
-  issue_v(0, tmk);
-  store_k<D>(kbuf[0], kreg);
+  // Prologue: K(0), V(0), K(1) into LDS, then S(0).  Paged source: a tile's
+  // page metadata is read from LDS when its loads are issued (carrying it
+  // one tile ahead in registers made the head-dim-128 kernel spill).
+  issue_k(0, meta(0));
+  issue_v(0, meta(0));
+  put_k(kbuf[0]);
   store_v<D, PAGED>(vbuf[0], vreg, kq, oc, v_active, PAGED ? L : kN);
   if (n_tiles > 1) {
-    tmv = meta(1);
-    issue_k(1, tmv);
-    store_k<D>(kbuf[1], kreg);
+    issue_k(1, meta(1));
+    put_k(kbuf[1]);
   }
-  if (n_tiles > 2) tmk = meta(2);
+  if constexpr (KDMA) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K tiles in LDS
   __syncthreads();
   f32x16 sA[2], sB[2];
   qk_block(sA[0], kbuf[0], 0);
@@ -630,19 +669,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   // K(t) and V(t-1), and one barrier publishes them.
 #define EKV_PREFILL_STEP(CUR, NXT)                                                              \
   {                                                                                             \
-    if (it + 2 < n_tiles) issue_k(it + 2, tmk);                                                 \
-    if (it + 1 < n_tiles) issue_v(it + 1, tmv);                                                 \
-    if constexpr (PAGED) {                                                                      \
-      tmv = tmk;                                                                                \
-      if (it + 3 < n_tiles) tmk = meta(it + 3);                                                 \
-    }                                                                                           \
+    if (it + 2 < n_tiles) issue_k(it + 2, meta(it + 2));                                        \
+    if (it + 1 < n_tiles) issue_v(it + 1, meta(it + 1));                                        \
     if (it < n_w) {                                                                             \
       if ((p.causal && it * kN + kN - 1 > r0) || (it * kN + kN > L)) mask_tile(CUR, it * kN);   \
       step(CUR, NXT, kbuf[(it + 1) & 1], vbuf[it & 1]);                                         \
     }                                                                                           \
-    if (it + 2 < n_tiles) store_k<D>(kbuf[it & 1], kreg);                                       \
+    if (it + 2 < n_tiles) put_k(kbuf[it & 1]);                                                  \
     if (it + 1 < n_tiles)                                                                       \
       store_v<D, PAGED>(vbuf[(it + 1) & 1], vreg, kq, oc, v_active, PAGED ? L - (it + 1) * kN : kN); \
+    if constexpr (KDMA) __builtin_amdgcn_s_waitcnt(0x0F70);                                     \
     __syncthreads();                                                                            \
     if (++it >= n_tiles) break;                                                                 \
   }
@@ -697,9 +733,6 @@ constexpr int kWsD = 128;
 constexpr int kWsWaves = 4;  // measured: 4 wavefronts (128 rows) beat 8 (256 rows) by 5%
 __host__ __device__ inline bool paged_route(const PrefillParams& p) { return p.page_table != nullptr; }
 
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, f16* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
-}
 
 __device__ __forceinline__ uint2 lds_tr16(const f16* p) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));

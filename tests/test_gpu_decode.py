@@ -100,6 +100,28 @@ def test_balanced_plan_ragged_empty_and_bad(hq, hkv, d):
     assert_close(outb[keep], want[keep])
 
 
+def test_one_split_plans_write_output_directly():
+    """Automatic plans that give every (sequence, KV head) one split: 8-wavefront
+    workgroups up to 256 groups, 4-wavefront ones from 512; the split kernel
+    writes out / lse itself (no merge), including empty sequences."""
+    for batch, lo, hi in ((32, 1, 4000), (64, 1, 200)):
+        step(f"decode one-split plan batch={batch}")
+        lens = np.random.default_rng(batch).integers(lo, hi, size=batch)
+        lens[3] = 0
+        c = synth.make_paged_case(400 + batch, lens, 32, 8, 128, compact_frac=0.5)
+        assert ekv().ekv_decode_scratch_bytes(batch, 32, 8, 128, c.max_seq_len, 0) == 0
+        dc = DeviceCase(c)
+        want, wlse = oracle_decode(c)
+        out, lse = dc.decode(torch.float32)
+        assert_close(out, want)
+        assert_lse_close(lse, wlse)
+        assert np.all(out[3] == 0) and np.all(np.isneginf(lse[3]))
+        out16, _ = dc.decode(torch.float16)
+        assert f16_bits_equal_rne(out16, out)
+        out_s, _ = dc.decode(torch.float32, pages_per_split=16)  # split + merge plan
+        assert max_abs(out_s, out) <= TOL
+
+
 def test_page_permutation_gives_identical_output():
     step("decode page permutation")
     c = synth.make_paged_case(9, [300, 129], 8, 2, 128, compact_frac=0.5, slack_frac=0.5)

@@ -11,32 +11,39 @@
 // This is a dense QK^T / PV contraction, so it runs on the matrix cores
 // (v_mfma_f32_32x32x16_f16, gfx950).  Workgroup = 128 query rows of one
 // query head of one prompt; wavefront w owns rows [32w, 32w+32).  Per 64-key
-// tile the workgroup stages K (row-major) and V^T (transposed on the way in)
-// in LDS, then each wavefront computes
+// tile each wavefront computes
 //     S^T[key][q] = K . Q^T      (A = K from LDS, B = Q in registers)
 //     O^T[d][q]  += V^T . P^T    (A = V^T from LDS, B = P^T in registers)
 // so that with the 32x32 output layout every per-query quantity (running max,
 // sum, rescale factor) lives in the lane whose column is that query: lane l
 // holds column l%32 and half of its rows; a single xor-32 exchange completes a
 // column reduction.  The key order inside the P.V contraction follows the
-// S^T register layout, and V^T is read in the same order.
+// S^T register layout, and V^T is read in the same order.  S of tile t + 1 is
+// computed in the same instruction stream as the softmax of tile t.
 // Launch order: workgroups are mapped so that each XCD (8 per MI355X, each
 // with its own L2) walks a contiguous range of (prompt, head, row tile), so
 // the K/V rows a head reuses stay in one L2; within a head the longest
 // (last) causal row tiles start first.
 //
-// Two sources of K/V, one compute loop:
-//   workspace rows  the gather route: contiguous FP16 rows per prompt;
-//   pages           the direct route ("Memory-Traffic Saturation ...",
-//                   section "Existing fallback: mixed-type prefill"; ElasticKV
-//                   section 3.2): the prompt's own page-table row, TARGET pages
-//                   as stored, compact pages' E4M3 values expanded while the
-//                   tile is staged, with the scaled gather's rounding
-//                   (fp16(fp32(e4m3) * fp32(scale))), so both routes feed the
-//                   MFMAs identical operands.
+// Two kernels, one arithmetic (identical operands and order, so their outputs
+// agree bit for bit):
+//   prefill_ws128_kernel  head dim 128 over workspace rows (the gather
+//                         route): K and V tiles go straight from memory into
+//                         swizzled LDS by buffer loads; V^T operands come
+//                         from transposing LDS reads.
+//   prefill_kernel        head dim 64 over workspace rows, and the direct
+//                         route over pages ("Memory-Traffic Saturation ...",
+//                         section "Existing fallback: mixed-type prefill";
+//                         ElasticKV section 3.2): the prompt's own page-table
+//                         row, TARGET pages as stored, compact pages' E4M3
+//                         values expanded while the tile is staged, with the
+//                         scaled gather's rounding (fp16(fp32(e4m3) *
+//                         fp32(scale))), so both routes feed the MFMAs
+//                         identical operands.  V^T is transposed with byte
+//                         permutes on its way into LDS.
 // A 64-key tile is 4 pages.  In the paged source each K chunk a thread loads
 // lies in a page that is uniform across its wavefront, and (head dim 128)
-// each wavefront stages the V of one page, so every load goes through a
+// each wavefront stages the K and V of one page, so every load goes through a
 // per-page buffer descriptor in scalar registers.
 #include "ekv_device.hpp"
 #include "ekv_internal.hpp"

@@ -112,12 +112,13 @@ int32_t ekv_decode_plan_pages_per_split(const int32_t* seq_lens_host, int32_t ba
 
 size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_seq_len, int32_t pages_per_split) {
-  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
-  if (pages_per_split == EKV_DECODE_BALANCED) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0) return 0;
+  if (pages_per_split == EKV_DECODE_BALANCED) {  // also for max_seq_len 0 (the merge writes empty rows)
     if (num_q_heads % num_kv_heads != 0) return 0;
     const int32_t n = ekv::decode_balanced_workgroups(batch, num_kv_heads, ceil_div(max_seq_len, EKV_PAGE_SIZE));
     return ekv::decode_balanced_scratch_bytes(n, num_q_heads, num_kv_heads, head_dim);
   }
+  if (max_seq_len == 0) return 0;
   const int32_t pps = pages_per_split > 0 ? pages_per_split
                                           : ekv_decode_pages_per_split(batch, num_kv_heads, max_seq_len);
   const int32_t splits = ceil_div(ceil_div(max_seq_len, EKV_PAGE_SIZE), pps);
@@ -202,7 +203,7 @@ ekv_status decode_impl(const ekv_paged_kv* kv, const void* q, int32_t batch, int
   p.max_seq_len = max_seq_len;
   p.pages_per_split = pps;
   p.n_splits = splits;
-  p.n_wg = max_pages > 0 ? n_wg : 0;
+  p.n_wg = n_wg;  // balanced plan (also when every sequence is empty: its merge writes them)
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   const size_t rows = balanced ? (size_t)n_wg * 2 * (num_q_heads / kv->num_kv_heads)
                                : (size_t)batch * num_q_heads * (size_t)splits;

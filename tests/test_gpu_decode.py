@@ -90,6 +90,12 @@ def test_balanced_plan_ragged_empty_and_bad(hq, hkv, d):
     w2, wl2 = oracle_decode(c2)
     assert_close(out2, w2)
     assert_lse_close(lse2, wl2)
+    # every sequence empty, max_seq_len 0: out 0, lse -inf
+    z = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
+    outz, lsez = dc.decode(torch.float32, pages_per_split=ekv().DECODE_BALANCED, seq_lens=z, max_seq_len=0)
+    assert np.all(outz == 0) and np.all(np.isneginf(lsez))
+    outz, lsez = dc.decode(torch.float32, seq_lens=z, max_seq_len=0)  # automatic plan
+    assert np.all(outz == 0) and np.all(np.isneginf(lsez))
     # one bad page id in sequence 6 (2053 tokens, cut over several ranges)
     bad = c.page_table.copy()
     bad[6, 70] = 1 << 20

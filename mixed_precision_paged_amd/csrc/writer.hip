@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kWriterThreads) void quantize_kernel(QuantizeParams
 // 2 dst and 2 dst + 1.  One workgroup per (pair, pool): every thread reads its
 // 16-byte chunks of both blocks and keeps their high bytes; a barrier; then
 // the writes, so dst may be a or b (in place).  blockIdx.y: 0 = K pool, 1 = V.
-constexpr int kPackMaxChunks = 8;  // 16-byte chunks of one block per thread (Hkv*D <= 2048)
+constexpr int kPackMaxUnits = 8;  // 32-byte units of one block per thread (Hkv*D <= 2048)
 
 __global__ __launch_bounds__(kWriterThreads) void pack_base_kernel(PackParams p) {
   const int pair = blockIdx.x;
@@ -190,28 +190,32 @@ __global__ __launch_bounds__(kWriterThreads) void pack_base_kernel(PackParams p)
   if ((unsigned)a >= (unsigned)p.n_target || (unsigned)b >= (unsigned)p.n_target ||
       (unsigned)d >= (unsigned)p.n_target)
     return;  // uniform for the workgroup: nothing is read or written
-  const int chunks = kPage * p.num_kv_heads * p.head_dim / 8;  // per block
-  const int64_t block_bytes = (int64_t)chunks * 16;
+  // a unit = 16 fp16 values (32 bytes) of a source block -> their 16 high
+  // bytes, one 16-byte store into each half of the destination block
+  const int units = kPage * p.num_kv_heads * p.head_dim / 16;
+  const int64_t block_bytes = (int64_t)units * 32;
   const uint4* pa = reinterpret_cast<const uint4*>(pool + a * block_bytes);
   const uint4* pb = reinterpret_cast<const uint4*>(pool + b * block_bytes);
-  uint2 ha[kPackMaxChunks], hb[kPackMaxChunks];
+  uint4 ha[kPackMaxUnits], hb[kPackMaxUnits];
 #pragma unroll
-  for (int j = 0; j < kPackMaxChunks; ++j) {
+  for (int j = 0; j < kPackMaxUnits; ++j) {
     const int c = threadIdx.x + kWriterThreads * j;
-    if (c < chunks) {
-      const uint4 x = pa[c], y = pb[c];
-      // bytes 1, 3, 5, 7 of each 8-byte half: the high bytes of 8 fp16 values
-      ha[j] = make_uint2(perm(x.y, x.x, 0x07050301u), perm(x.w, x.z, 0x07050301u));
-      hb[j] = make_uint2(perm(y.y, y.x, 0x07050301u), perm(y.w, y.z, 0x07050301u));
+    if (c < units) {
+      const uint4 x0 = pa[2 * c], x1 = pa[2 * c + 1], y0 = pb[2 * c], y1 = pb[2 * c + 1];
+      // bytes 1, 3, 5, 7 of each 8-byte half: the high bytes of 4 fp16 values
+      ha[j] = make_uint4(perm(x0.y, x0.x, 0x07050301u), perm(x0.w, x0.z, 0x07050301u),
+                         perm(x1.y, x1.x, 0x07050301u), perm(x1.w, x1.z, 0x07050301u));
+      hb[j] = make_uint4(perm(y0.y, y0.x, 0x07050301u), perm(y0.w, y0.z, 0x07050301u),
+                         perm(y1.y, y1.x, 0x07050301u), perm(y1.w, y1.z, 0x07050301u));
     }
   }
   __syncthreads();
-  uint2* out0 = reinterpret_cast<uint2*>(pool + d * block_bytes);
-  uint2* out1 = reinterpret_cast<uint2*>(pool + d * block_bytes + block_bytes / 2);
+  uint4* out0 = reinterpret_cast<uint4*>(pool + d * block_bytes);
+  uint4* out1 = reinterpret_cast<uint4*>(pool + d * block_bytes + block_bytes / 2);
 #pragma unroll
-  for (int j = 0; j < kPackMaxChunks; ++j) {
+  for (int j = 0; j < kPackMaxUnits; ++j) {
     const int c = threadIdx.x + kWriterThreads * j;
-    if (c < chunks) {
+    if (c < units) {
       out0[c] = ha[j];
       out1[c] = hb[j];
     }
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(kWriterThreads) void pack_base_kernel(PackParams p)
 
 hipError_t launch_pack_base(const PackParams& p, hipStream_t stream) {
   if (p.n_pairs == 0) return hipSuccess;
-  if (kPage * p.num_kv_heads * p.head_dim / 8 > kPackMaxChunks * kWriterThreads) return hipErrorInvalidValue;
+  if (kPage * p.num_kv_heads * p.head_dim / 16 > kPackMaxUnits * kWriterThreads) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pack_base_kernel, dim3((unsigned)p.n_pairs, 2), dim3(kWriterThreads), 0, stream, p);
   return hipGetLastError();
 }

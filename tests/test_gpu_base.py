@@ -40,7 +40,7 @@ def _oracle(case):
 def test_pack_pairs_bit_exact_in_place_and_skips():
     step("pack BASE pairs")
     rng = np.random.default_rng(60)
-    for hkv, d in ((8, 128), (1, 64), (2, 64)):
+    for hkv, d in ((8, 128), (1, 64), (2, 64), (16, 128), (3, 64)):  # Hkv*D up to the 2048 limit
         n = 12
         k = synth.normal_fp16(rng, (n, 16, hkv, d))
         v = synth.normal_fp16(rng, (n, 16, hkv, d))

@@ -286,7 +286,7 @@ def bench_prefill(args):
         "gather": {"avg_chunk_us": round(g * 1e6, 1), "bytes_per_chunk": rd + wr,
                    "gbps": round((rd + wr) / g / 1e9, 1), "peak_gbps": HBM_PEAK_GBPS,
                    "frac": round((rd + wr) / g / 1e9 / HBM_PEAK_GBPS, 4)},
-        "direct_paged": {"kernel": "ekv_prefill_paged_attention (prefill_kernel<128, paged>)",
+        "direct_paged": {"kernel": "ekv_prefill_paged_attention (prefill_ws128_kernel, paged source)",
                          "prompts_per_launch": 32, "avg_ms": round(d * 1e3, 3),
                          "tflops": round(4 * flops / d / 1e12, 1),
                          "mfma_frac": round(4 * flops / d / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),

@@ -26,25 +26,23 @@
 // (last) causal row tiles start first.
 //
 // Two kernels, one arithmetic (identical operands and order, so their outputs
-// agree bit for bit):
-//   prefill_ws128_kernel  head dim 128 over workspace rows (the gather
-//                         route): K and V tiles go straight from memory into
-//                         swizzled LDS by buffer loads; V^T operands come
-//                         from transposing LDS reads.
-//   prefill_kernel        head dim 64 over workspace rows, and the direct
-//                         route over pages ("Memory-Traffic Saturation ...",
-//                         section "Existing fallback: mixed-type prefill";
-//                         ElasticKV section 3.2): the prompt's own page-table
-//                         row, TARGET pages as stored, compact pages' E4M3
-//                         values expanded while the tile is staged, with the
-//                         scaled gather's rounding (fp16(fp32(e4m3) *
-//                         fp32(scale))), so both routes feed the MFMAs
-//                         identical operands.  V^T is transposed with byte
-//                         permutes on its way into LDS.
-// A 64-key tile is 4 pages.  In the paged source each K chunk a thread loads
-// lies in a page that is uniform across its wavefront, and (head dim 128)
-// each wavefront stages the K and V of one page, so every load goes through a
-// per-page buffer descriptor in scalar registers.
+// agree bit for bit).  Sources: the gather workspace, or the direct route over
+// pages ("Memory-Traffic Saturation ...", section "Existing fallback:
+// mixed-type prefill"; ElasticKV section 3.2): the prompt's own page-table
+// row, TARGET pages as stored, compact pages' E4M3 values expanded while the
+// tile is staged with the scaled gather's rounding (fp16(fp32(e4m3) *
+// fp32(scale))), so both routes feed the MFMAs identical operands.
+//   prefill_ws128_kernel  head dim 128, both sources: K and V tiles go
+//                         straight from memory into swizzled LDS by buffer
+//                         loads; V^T operands come from transposing LDS
+//                         reads.  Paged: wavefront w stages page w of each
+//                         64-key tile through per-page descriptors; a
+//                         compact page's codes land in a per-wavefront LDS
+//                         area and are expanded into the V tile before the
+//                         barrier that publishes it.
+//   prefill_kernel        head dim 64, both sources: K and V staged through
+//                         registers; V^T transposed with byte permutes on its
+//                         way into padded LDS tiles.
 #include "ekv_device.hpp"
 #include "ekv_internal.hpp"
 
@@ -161,9 +159,8 @@ __device__ __forceinline__ void store_v(SmemV<D>& s, const VRegs& r, int kq, int
                                         int valid_keys) {
   if (v_active) {
     uint4 v[4];
-    // head dim 128: the page kind is wave-uniform (a branch); head dim 64: the
-    // two half-wavefronts may hold different pages (a select)
-    const bool codes = D == 128 ? (bool)__builtin_amdgcn_readfirstlane((int)r.v_codes) : r.v_codes;
+    // the two half-wavefronts may hold different pages (a select)
+    const bool codes = r.v_codes;
     if (codes) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = expand8(r.vlo[i], r.vscale);
@@ -240,15 +237,6 @@ __device__ __forceinline__ TileMeta uniform_meta(const TileMetaRaw& r) {
   return t;
 }
 
-// Entry k of the tile metadata for a wave-uniform runtime k (selects, so the
-// arrays stay in registers).
-__device__ __forceinline__ int tm_meta(const TileMeta& t, int k) {
-  return k == 0 ? t.m[0] : k == 1 ? t.m[1] : k == 2 ? t.m[2] : t.m[3];
-}
-__device__ __forceinline__ float tm_scale(const TileMeta& t, int k) {
-  return k == 0 ? t.s[0] : k == 1 ? t.s[1] : k == 2 ? t.s[2] : t.s[3];
-}
-
 // Descriptors of one page (meta = (phys << 1) | kind, always a valid page:
 // pages past the prompt were staged as a copy of its page 0).  Each range is
 // one head's page; rows past the prompt end are masked (K) or zeroed (V) in
@@ -295,28 +283,19 @@ __device__ __forceinline__ void load_v_page(uint2* lo, uint2* hi, const PageDesc
   }
 }
 
-// Paged loads of tile t (keys 64 t .. 64 t + 63 = prompt pages 4 t .. 4 t + 3).
-// K chunk i of this thread lies in tile page D == 128 ? i : 2 i + wave / 2;
-// the V unit's page is the wavefront (D 128) or the half-wavefront (D 64).
+// Paged loads of tile t (keys 64 t .. 64 t + 63 = prompt pages 4 t .. 4 t + 3),
+// head dim 64.  K chunk i of this thread lies in tile page 2 i + wave / 2; the
+// V unit's page is that of its half-wavefront.
 template <int D>
 __device__ __forceinline__ void load_k_paged(KRegs<D>& r, PagedSrc src, const TileMetaRaw& raw, int wave,
                                              uint32_t koff) {
   const TileMeta tm = uniform_meta(raw);
-  if constexpr (D == 128) {
+  const bool hi = wave >> 1;
 #pragma unroll
-    for (int i = 0; i < KRegs<D>::KCH; ++i) {
-      const PageDesc pd = page_desc(src, tm.m[i], tm.s[i]);
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pd.k, koff, 0, 0);
-      r.k[i] = make_uint4(x.x, x.y, x.z, x.w);
-    }
-  } else {  // chunk i lies in page 2i + wave/2: a choice of two
-    const bool hi = wave >> 1;
-#pragma unroll
-    for (int i = 0; i < KRegs<D>::KCH; ++i) {
-      const PageDesc pd = page_desc(src, hi ? tm.m[2 * i + 1] : tm.m[2 * i], hi ? tm.s[2 * i + 1] : tm.s[2 * i]);
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pd.k, koff, 0, 0);
-      r.k[i] = make_uint4(x.x, x.y, x.z, x.w);
-    }
+  for (int i = 0; i < KRegs<D>::KCH; ++i) {
+    const PageDesc pd = page_desc(src, hi ? tm.m[2 * i + 1] : tm.m[2 * i], hi ? tm.s[2 * i + 1] : tm.s[2 * i]);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pd.k, koff, 0, 0);
+    r.k[i] = make_uint4(x.x, x.y, x.z, x.w);
   }
 }
 
@@ -324,12 +303,7 @@ template <int D>
 __device__ __forceinline__ void load_v_paged(VRegs& r, PagedSrc src, const TileMetaRaw& raw, int wave, int lane,
                                              uint32_t voff16, uint32_t voff8) {
   const TileMeta tm = uniform_meta(raw);
-  if constexpr (D == 128) {
-    const PageDesc pd = page_desc(src, tm_meta(tm, wave), tm_scale(tm, wave));
-    load_v_page(r.vlo, r.vhi, pd, src, voff16, voff8);
-    r.v_codes = pd.codes;
-    r.vscale = pd.scale;
-  } else if (wave < 2) {  // D 64: 128 V units, two pages per wavefront
+  if (wave < 2) {  // 128 V units, two pages per wavefront
     const bool w1 = wave == 1;
     const PageDesc pa = page_desc(src, w1 ? tm.m[2] : tm.m[0], w1 ? tm.s[2] : tm.s[0]);
     const PageDesc pb = page_desc(src, w1 ? tm.m[3] : tm.m[1], w1 ? tm.s[3] : tm.s[1]);
@@ -365,15 +339,50 @@ __device__ void write_nan_rows(const PrefillParams& p, int64_t q0, int r_lo, int
   }
 }
 
+// Paged source: stages the prompt's page ids, kinds and scales of pages
+// 0 .. n_pages - 1 in LDS (meta = (phys << 1) | kind; scale 1 for a TARGET
+// page).  Pages past the prompt get a copy of page 0, which is in bounds:
+// their keys are masked and their values zeroed in the tile.  Returns false
+// (the same on every thread) if a page id lies outside its pool or a flag is
+// unknown; the caller then writes its rows as NaN.
+__device__ bool stage_page_meta(const PrefillParams& p, int prompt, int g, int L, int n_pages, int* s_meta,
+                                float* s_scale, int* s_bad) {
+  if (threadIdx.x == 0) *s_bad = 0;
+  __syncthreads();
+  const int64_t pt_row = (int64_t)prompt * p.pt_stride;
+  for (int j = threadIdx.x; j < n_pages; j += blockDim.x) {
+    int meta = -2;
+    float sc = 1.0f;
+    if (kPage * j < L) {
+      const int id = p.page_table[pt_row + j];
+      const int kind = p.fidelity ? (int)p.fidelity[pt_row + j] : p.uniform_kind;
+      const int n_pool = kind == 1 ? p.n_compact : p.n_target;
+      if ((kind == 0 || kind == 1) && id >= 0 && id < n_pool) {
+        meta = (id << 1) | kind;
+        if (kind == 1) sc = p.v_scale[(int64_t)id * p.num_kv_heads + g];
+      } else {
+        *s_bad = 1;
+      }
+    }
+    s_meta[j] = meta;
+    s_scale[j] = sc;
+  }
+  __syncthreads();
+  if (*s_bad) return false;
+  for (int j = threadIdx.x; j < n_pages; j += blockDim.x)
+    if (kPage * j >= L) {
+      s_meta[j] = s_meta[0];
+      s_scale[j] = s_scale[0];
+    }
+  __syncthreads();
+  return true;
+}
+
 template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, int n_mtiles) {
+  static_assert(D == 64, "head dim 128 runs prefill_ws128_kernel");
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  // Paged source, head dim 128: K tiles go from the pages straight into LDS
-  // (wavefront w stages page w of the tile, 4 row quads of 1 KiB), unpadded
-  // with 16-byte chunk c of row r at chunk c ^ (r % 16), as in the workspace
-  // kernel; no K staging registers.
-  constexpr bool KDMA = PAGED && D == 128;
   // K of tiles i + 1 (computing S ahead) and i + 2 (being stored), V of
   // tiles i (P.V) and i + 1 (being stored)
   __shared__ SmemK<D> kbuf[2];
@@ -424,42 +433,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
 
   PagedSrc src{};
   if constexpr (PAGED) {
-    // stage page ids, kinds and scales of pages 0 .. 4 n_tiles - 1; a page
-    // past the prompt gets -2 (reads zeros); an out-of-pool id or unknown flag
-    // marks the row tile bad (its rows are written as NaN)
-    if (threadIdx.x == 0) s_bad = 0;
-    __syncthreads();
-    const int64_t pt_row = (int64_t)prompt * p.pt_stride;
-    for (int j = threadIdx.x; j < 4 * n_tiles; j += kThreads) {
-      int meta = -2;
-      float sc = 1.0f;
-      if (kPage * j < L) {
-        const int id = p.page_table[pt_row + j];
-        const int kind = p.fidelity ? (int)p.fidelity[pt_row + j] : p.uniform_kind;
-        const int n_pool = kind == 1 ? p.n_compact : p.n_target;
-        if ((kind == 0 || kind == 1) && id >= 0 && id < n_pool) {
-          meta = (id << 1) | kind;
-          if (kind == 1) sc = p.v_scale[(int64_t)id * p.num_kv_heads + g];
-        } else {
-          s_bad = 1;
-        }
-      }
-      s_meta[j] = meta;
-      s_scale[j] = sc;
-    }
-    __syncthreads();
-    if (s_bad) {
+    // page ids, kinds and scales of pages 0 .. 4 n_tiles - 1; an out-of-pool
+    // id or unknown flag marks the row tile bad (its rows are written as NaN)
+    if (!stage_page_meta(p, prompt, g, L, 4 * n_tiles, s_meta, s_scale, &s_bad)) {
       write_nan_rows<D>(p, q0, m0, min(L, m0 + kM), h);
       return;
     }
-    // pages past the prompt: a copy of page 0 (in bounds; their keys are masked
-    // and their values zeroed in the tile)
-    for (int j = threadIdx.x; j < 4 * n_tiles; j += kThreads)
-      if (kPage * j >= L) {
-        s_meta[j] = s_meta[0];
-        s_scale[j] = s_scale[0];
-      }
-    __syncthreads();
     src.kt = reinterpret_cast<const char*>(p.k_target) + (int64_t)g * D * 2;
     src.vt = reinterpret_cast<const char*>(p.v_target) + (int64_t)g * D * 2;
     src.kc = reinterpret_cast<const char*>(p.k_compact) + (int64_t)g * D * 2;
@@ -489,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
 
   // Per-lane load offsets.  V unit (kq, oc): workspace source kq = t % 16
   // (consecutive lanes take consecutive key quads); paged source kq = t / (D/8),
-  // so a wavefront's units share one page (D 128) or two (D 64).
+  // so a wavefront's units share two pages.
   constexpr int units = (kN / 4) * (D / 8);
   const bool v_active = threadIdx.x < units;
   const int vt_id = v_active ? threadIdx.x : 0;
@@ -501,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   uint32_t pkoff = 0, pvoff16 = 0, pvoff8 = 0;
   if constexpr (PAGED) {
     // K chunk i: key t/(D/8) + (256/(D/8)) i, i.e. the same slot of tile page
-    // D == 128 ? i : 2i + wave/2; V rows 4(kq%4) .. +3 of tile page kq/4
+    // 2i + wave/2; V rows 4(kq%4) .. +3 of tile page kq/4
     pkoff = (uint32_t)((threadIdx.x / (D / 8)) % kPage) * rowb + 16u * (threadIdx.x % (D / 8));
     pvoff16 = (uint32_t)(4 * (kq % 4)) * rowb + 16u * oc;
     pvoff8 = (uint32_t)(4 * (kq % 4)) * src.rowb8 + 8u * oc;
@@ -526,40 +505,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   vreg.v_codes = false;
   vreg.vscale = 1.0f;
 
-  // KDMA: this lane's row quad j of its wavefront's page: row 4 j + l / 16,
-  // swizzled chunk l % 16 holds source chunk (l % 16) ^ row
-  uint32_t kdo[4] = {0u, 0u, 0u, 0u};
-  if constexpr (KDMA) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * j + (lane >> 4);
-      kdo[j] = (uint32_t)r * rowb + 16u * (uint32_t)((lane & 15) ^ r);
-    }
-  }
   auto issue_k = [&](int t, const TileMetaRaw& tm) {
-    if constexpr (KDMA) {
-      const TileMeta um = uniform_meta(tm);
-      const PageDesc pd = page_desc(src, tm_meta(um, wave_u), tm_scale(um, wave_u));
-      f16* dst = kbuf[t & 1].k + 16 * wave_u * D;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lds_dma16(pd.k, dst + 4 * j * D, kdo[j]);
-    } else if constexpr (PAGED) {
-      load_k_paged<D>(kreg, src, tm, wave_u, pkoff);
-    } else {
-      load_k<D>(kreg, kr, koff, (uint32_t)(t * kN) * rowb);
-    }
+    if constexpr (PAGED) load_k_paged<D>(kreg, src, tm, wave_u, pkoff);
+    else load_k<D>(kreg, kr, koff, (uint32_t)(t * kN) * rowb);
   };
-  // K tile to LDS: KDMA tiles are already there (their loads are waited for
-  // before the barrier that publishes them)
-  auto put_k = [&](SmemK<D>& sk) {
-    if constexpr (!KDMA) store_k<D>(sk, kreg);
-  };
+  auto put_k = [&](SmemK<D>& sk) { store_k<D>(sk, kreg); };
   // QK^T A-operand offsets (halves) of k-step ks inside a 32-row key block
   uint32_t kro[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    kro[ks] = KDMA ? (uint32_t)col * D + 8u * (uint32_t)((2 * ks + half) ^ (col & 15))
-                   : (uint32_t)col * SmemK<D>::kStride + 8u * (uint32_t)half + 16u * (uint32_t)ks;
+    kro[ks] = (uint32_t)col * SmemK<D>::kStride + 8u * (uint32_t)half + 16u * (uint32_t)ks;
   auto issue_v = [&](int t, const TileMetaRaw& tm) {
     if constexpr (PAGED) load_v_paged<D>(vreg, src, tm, wave_u, lane, pvoff16, pvoff8);
     else load_v(vreg, vr, voff, (uint32_t)(t * kN) * rowb);
@@ -576,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   // S^T = K . Q^T of one 32-key block of a tile (8 MFMAs over the head dim)
   auto qk_block = [&](f32x16& sacc, const SmemK<D>& sk, int kb) {
     sacc = f32x16{};
-    const f16* kp = &sk.k[kb * 32 * (KDMA ? D : SmemK<D>::kStride)];
+    const f16* kp = &sk.k[kb * 32 * SmemK<D>::kStride];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const f16x8 a = *reinterpret_cast<const f16x8*>(kp + kro[ks]);
@@ -664,7 +619,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
     issue_k(1, meta(1));
     put_k(kbuf[1]);
   }
-  if constexpr (KDMA) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K tiles in LDS
   __syncthreads();
   f32x16 sA[2], sB[2];
   qk_block(sA[0], kbuf[0], 0);
@@ -685,7 +639,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
     if (it + 2 < n_tiles) put_k(kbuf[it & 1]);                                                  \
     if (it + 1 < n_tiles)                                                                       \
       store_v<D, PAGED>(vbuf[(it + 1) & 1], vreg, kq, oc, v_active, PAGED ? L - (it + 1) * kN : kN); \
-    if constexpr (KDMA) __builtin_amdgcn_s_waitcnt(0x0F70);                                     \
     __syncthreads();                                                                            \
     if (++it >= n_tiles) break;                                                                 \
   }
@@ -719,9 +672,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   if (p.lse && half == 0) p.lse[qrow * p.num_q_heads + h] = (m + log2f(l)) * kLn2;
 }
 
-// Head dim 128 over workspace rows: the same flash loop with the K and V
+// Head dim 128, workspace rows or pages: the same flash loop with the K and V
 // tiles staged by buffer loads straight into LDS (no staging registers, no
-// LDS stores) and V^T operands read with gfx950 transposing LDS reads.
+// LDS stores for K and for fp16 V) and V^T operands read with gfx950
+// transposing LDS reads.
 //   LDS tiles are row-major, 256 B per key row, 16-byte chunks swizzled:
 //   K chunk c of row r sits at chunk c ^ (r % 16): the 16 rows one
 //   ds_read_b128 pass touches hit 16 distinct bank groups.  V chunk c of row
@@ -749,10 +703,13 @@ __device__ __forceinline__ uint2 lds_tr16(const f16* p) {
 }
 
 // NW wavefronts, 32 NW query rows per workgroup, sharing every staged tile.
-template <int NW>
+// PAGED: keys and values come from the prompt's pages (4 wavefronts: each
+// stages the K and V of one page of the tile).
+template <int NW, bool PAGED>
 __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillParams p, int n_mtiles) {
   constexpr int D = kWsD;
   constexpr int QUADS = 16 / NW;  // K (and V) row quads each wavefront stages per tile
+  static_assert(!PAGED || QUADS * 4 == kPage, "paged staging: one page per wavefront");
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   constexpr int TILE = kN * D;  // halves per K or V tile
@@ -760,6 +717,12 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
   // tiles t (P.V) and t + 1 (being staged)
   __shared__ __attribute__((aligned(1024))) f16 kbuf[2 * TILE];
   __shared__ __attribute__((aligned(1024))) f16 vbuf[2 * TILE];
+  // paged source: E4M3 codes of the compact page each wavefront stages, and
+  // the prompt's page metadata
+  __shared__ __attribute__((aligned(16))) uint8_t vcodes[PAGED ? NW * kPage * D : 16];
+  __shared__ __attribute__((aligned(16))) int s_meta[PAGED ? kMaxPromptPages : 4];
+  __shared__ __attribute__((aligned(16))) float s_scale[PAGED ? kMaxPromptPages : 4];
+  __shared__ int s_bad;
 
   // XCD-aware work mapping (as in prefill_kernel).
   const int total = (int)(gridDim.x);
@@ -777,8 +740,10 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
   if (q0 < 0 || q1 < q0 || q1 > p.q_rows) return;  // rows not addressable: nothing to write
   const int L = q1 - q0;
   const int m0 = mt * 32 * NW;
-  const int kv0 = p.kv_start[prompt];
-  const bool ok = L <= p.max_len && kv0 >= 0 && (int64_t)kv0 + L <= p.kv_rows;
+  const int kv0 = PAGED ? 0 : p.kv_start[prompt];
+  const bool ok = PAGED ? (L <= p.max_len && L <= kMaxPromptPages * kPage &&
+                           (int64_t)L <= (int64_t)p.pt_stride * kPage)
+                        : (L <= p.max_len && kv0 >= 0 && (int64_t)kv0 + L <= p.kv_rows);
   if (!ok) {
     if (mt == 0) write_nan_rows<D>(p, q0, 0, L, h);
     return;
@@ -796,31 +761,104 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
   const int n_tiles = (n_end + kN - 1) / kN;
   const int n_w = p.causal ? min(n_tiles, (r0 + 31) / kN + 1) : n_tiles;
   const uint32_t rowb = (uint32_t)p.num_kv_heads * D * 2u;
+  const uint32_t rowb8 = (uint32_t)p.num_kv_heads * D;  // E4M3 row (paged source)
 
-  // descriptors over this prompt's K/V rows of KV head g
+  if constexpr (PAGED) {
+    // page ids, kinds and scales of pages 0 .. 4 n_tiles - 1; an out-of-pool
+    // id or unknown flag marks the row tile bad (its rows are written as NaN)
+    if (!stage_page_meta(p, prompt, g, L, 4 * n_tiles, s_meta, s_scale, &s_bad)) {
+      write_nan_rows<D>(p, q0, m0, min(L, m0 + 32 * NW), h);
+      return;
+    }
+  }
+
+  // workspace source: descriptors over this prompt's K/V rows of KV head g
+  // (rows past the prompt read as zeros); paged source: pool bases at head g
   const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2u;
-  const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
-  const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
+  const char* kbase = reinterpret_cast<const char*>(PAGED ? p.k_target : p.k) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
+  const char* vbase = reinterpret_cast<const char*>(PAGED ? p.v_target : p.v) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
+  const char* kcbase = reinterpret_cast<const char*>(p.k_compact) + (int64_t)g * D * 2;
+  const char* vcbase = reinterpret_cast<const char*>(p.v_compact) + (int64_t)g * D;
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, span, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, span, kBufferFlags);
 
   // staging: row quad j of this wavefront = tile rows 4 (QUADS wave + j) .. + 3
+  // (paged: rows 4 j .. + 3 of the wavefront's page; offsets within the page)
   uint32_t kso[QUADS], vso[QUADS];
 #pragma unroll
   for (int j = 0; j < QUADS; ++j) {
     const int r = 4 * (QUADS * wave + j) + (lane >> 4), pc = lane & 15;
-    kso[j] = (uint32_t)r * rowb + 16u * (uint32_t)(pc ^ (r & 15));
-    vso[j] = (uint32_t)r * rowb + 16u * (uint32_t)(pc ^ (4 * (r & 3)));
+    const int rs = PAGED ? r % kPage : r;
+    kso[j] = (uint32_t)rs * rowb + 16u * (uint32_t)(pc ^ (r & 15));
+    vso[j] = (uint32_t)rs * rowb + 16u * (uint32_t)(pc ^ (4 * (r & 3)));
   }
+  // paged compact V: lane l takes 16 codes of page row 8 c + l / 8 (c = 0, 1)
+  uint32_t cso[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) cso[c] = (uint32_t)(8 * c + (lane >> 3)) * rowb8 + 16u * (uint32_t)(lane & 7);
+  auto page_meta = [&](int j) { return __builtin_amdgcn_readfirstlane(s_meta[j]); };
   auto stage_k = [&](int t, int b) {
-    const uint32_t to = (uint32_t)(t * kN) * rowb;
+    if constexpr (PAGED) {
+      const int meta = page_meta(4 * t + wave);
+      const char* base = ((meta & 1) ? kcbase : kbase) + (int64_t)(meta >> 1) * kPage * rowb;
+      const __amdgpu_buffer_rsrc_t kd = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)base, (short)0, (kPage - 1) * rowb + D * 2u, kBufferFlags);
 #pragma unroll
-    for (int j = 0; j < QUADS; ++j) lds_dma16(kr, &kbuf[b * TILE + 4 * (QUADS * wave + j) * D], kso[j] + to);
+      for (int j = 0; j < QUADS; ++j) lds_dma16(kd, &kbuf[b * TILE + 4 * (QUADS * wave + j) * D], kso[j]);
+    } else {
+      const uint32_t to = (uint32_t)(t * kN) * rowb;
+#pragma unroll
+      for (int j = 0; j < QUADS; ++j) lds_dma16(kr, &kbuf[b * TILE + 4 * (QUADS * wave + j) * D], kso[j] + to);
+    }
   };
+  // Paged: a TARGET page's values go straight to the tile; a compact page's
+  // codes go to this wavefront's staging area and are expanded by put_v.
+  // The descriptors end at the prompt's last row, so later rows read zeros.
   auto stage_v = [&](int t, int b) {
-    const uint32_t to = (uint32_t)(t * kN) * rowb;
+    if constexpr (PAGED) {
+      const int pj = 4 * t + wave;
+      const int meta = page_meta(pj);
+      const uint32_t valid = (uint32_t)min(max(L - kPage * pj, 0), kPage);
+      const int64_t phys = meta >> 1;
+      if (meta & 1) {
+        const __amdgpu_buffer_rsrc_t vd = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vcbase + phys * kPage * rowb8), (short)0, valid ? (valid - 1) * rowb8 + D : 0u, kBufferFlags);
 #pragma unroll
-    for (int j = 0; j < QUADS; ++j) lds_dma16(vr, &vbuf[b * TILE + 4 * (QUADS * wave + j) * D], vso[j] + to);
+        for (int c = 0; c < 2; ++c)
+          lds_dma16(vd, reinterpret_cast<f16*>(&vcodes[wave * kPage * D + 1024 * c]), cso[c]);
+      } else {
+        const __amdgpu_buffer_rsrc_t vd = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vbase + phys * kPage * rowb), (short)0, valid ? (valid - 1) * rowb + D * 2u : 0u, kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < QUADS; ++j) lds_dma16(vd, &vbuf[b * TILE + 4 * (QUADS * wave + j) * D], vso[j]);
+      }
+    } else {
+      const uint32_t to = (uint32_t)(t * kN) * rowb;
+#pragma unroll
+      for (int j = 0; j < QUADS; ++j) lds_dma16(vr, &vbuf[b * TILE + 4 * (QUADS * wave + j) * D], vso[j] + to);
+    }
+  };
+  // Paged compact page (after its codes have landed): lane l expands the 32
+  // codes of page row l / 4, d 32 (l % 4) .. + 31, with the gather's rounding
+  // (fp16(fp32(code) * fp32(scale))) into the swizzled V tile.
+  auto put_v = [&](int t, int b) {
+    if constexpr (PAGED) {
+      const int pj = 4 * t + wave;
+      if (page_meta(pj) & 1) {
+        const float sc = rfl(s_scale[pj]);
+        const int r = lane >> 2, sg = lane & 3;
+        const uint8_t* cs = &vcodes[wave * kPage * D + r * D + 32 * sg];
+        const uint4 c0 = *reinterpret_cast<const uint4*>(cs);
+        const uint4 c1 = *reinterpret_cast<const uint4*>(cs + 16);
+        const int R = kPage * wave + r;
+        f16* row = &vbuf[b * TILE + R * D];
+        const int sw = 4 * (R & 3);
+        *reinterpret_cast<uint4*>(row + 8 * ((4 * sg + 0) ^ sw)) = expand8(make_uint2(c0.x, c0.y), sc);
+        *reinterpret_cast<uint4*>(row + 8 * ((4 * sg + 1) ^ sw)) = expand8(make_uint2(c0.z, c0.w), sc);
+        *reinterpret_cast<uint4*>(row + 8 * ((4 * sg + 2) ^ sw)) = expand8(make_uint2(c1.x, c1.y), sc);
+        *reinterpret_cast<uint4*>(row + 8 * ((4 * sg + 3) ^ sw)) = expand8(make_uint2(c1.z, c1.w), sc);
+      }
+    }
   };
 
   // QK^T A operand: K row kb*32 + col, chunk 2 ks + half at chunk (2 ks + half) ^ (col % 16)
@@ -920,6 +958,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
   stage_v(0, 0);
   if (n_tiles > 1) stage_k(1, 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's tile loads have landed
+  put_v(0, 0);
   __syncthreads();
   f32x16 sA[2], sB[2];
   qk_block(sA[0], 0, 0);
@@ -937,6 +976,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
       step(CUR, NXT, (it + 1) & 1, it & 1);                                                     \
     }                                                                                           \
     __builtin_amdgcn_s_waitcnt(0x0F70);                                                         \
+    if (it + 1 < n_tiles) put_v(it + 1, (it + 1) & 1);                                          \
     __syncthreads();                                                                            \
     if (++it >= n_tiles) break;                                                                 \
   }
@@ -977,18 +1017,19 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const int n_mtiles = (p.max_len + kM - 1) / kM;
   const int64_t blocks = (int64_t)n_mtiles * p.num_q_heads * p.n_prompts;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (p.head_dim == kWsD && !paged_route(p)) {
+  const bool paged = paged_route(p);
+  if (paged && p.max_len > kMaxPromptPages * kPage) return hipErrorInvalidValue;
+  if (p.head_dim == kWsD) {
     constexpr int NW = kWsWaves;
     const int n_mt = (p.max_len + 32 * NW - 1) / (32 * NW);
     const int64_t nb = (int64_t)n_mt * p.num_q_heads * p.n_prompts;
-    hipLaunchKernelGGL(prefill_ws128_kernel<NW>, dim3((unsigned)nb), dim3(NW * kWave), 0, stream, p, n_mt);
+    if (paged)
+      hipLaunchKernelGGL((prefill_ws128_kernel<NW, true>), dim3((unsigned)nb), dim3(NW * kWave), 0, stream, p, n_mt);
+    else
+      hipLaunchKernelGGL((prefill_ws128_kernel<NW, false>), dim3((unsigned)nb), dim3(NW * kWave), 0, stream, p, n_mt);
     return hipGetLastError();
   }
-  const bool paged = p.page_table != nullptr;
-  if (paged && p.max_len > kMaxPromptPages * kPage) return hipErrorInvalidValue;
-  if (p.head_dim == 128 && paged) {
-    hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, p, n_mtiles);
-  } else if (p.head_dim == 64) {
+  if (p.head_dim == 64) {
     if (paged) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, block, 0, stream, p, n_mtiles);
     else hipLaunchKernelGGL((prefill_kernel<64, false>), grid, block, 0, stream, p, n_mtiles);
   } else {

@@ -4,8 +4,13 @@ Decode: every output element against the oracle.  Gather: bit-exact on a full
 4,096-page chunk.  Prefill: sampled rows (tile boundaries, first/last rows,
 random rows) per prompt, every head, against the oracle row by row.  Mixed
 batch: one layer routed into one output tensor, decode rows fully checked,
-prefill rows sampled, and every row written by exactly its own path.
+prefill rows sampled, and every row written by exactly its own path; the same
+for all 36 layers on request (EKV_ALL_LAYERS=1).
 """
+import concurrent.futures
+import multiprocessing
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -94,10 +99,10 @@ def test_compact_prefill_32x8192_in_four_chunks():
         del out, lse, q
 
 
-def test_mixed_batch_one_layer_routed():
-    """Decode rows 0..31 and prefill rows 32.. of one layer land in one output tensor."""
-    step("fullsize mixed batch layer 0: gather -> prefill -> decode")
-    L = synth.mixed_batch_layer(0)
+def _check_routed_layer(L, seed):
+    """Route one mixed-batch layer into one output tensor (gather -> prefill into rows
+    n_decode.., then decode into rows 0..n_decode-1) and check it against the oracle:
+    every decode row, sampled prefill rows, and every row written by its own path."""
     c = L.paged
     dc = DeviceCase(c)
     H, D, Hq = c.num_kv_heads, c.head_dim, c.num_q_heads
@@ -122,13 +127,14 @@ def test_mixed_batch_one_layer_routed():
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     ls = lse.cpu().numpy()
+    del out, lse, ws_k, ws_v, dc
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(ls)), "every row written by its own path"
     want, wlse = oracle.decode_attention(L.q_decode, c.k_target, c.v_target, c.k_compact, c.v_compact,
                                          c.v_scale, c.page_table[:nd], c.fidelity[:nd], lens, c.sm_scale)
     assert_close(o[:nd], want, what="decode rows")
     assert_lse_close(ls[:nd], wlse)
     wk, wv = oracle.gather_compact_pages(c.k_compact, c.v_compact, c.v_scale, ids, True)
-    rng = np.random.default_rng(5)
+    rng = np.random.default_rng(seed)
     sample = []
     for i in range(len(prompts)):
         sample += [int(L.cu_seqlens_q[i]) + r for r in _sample_rows(int(L.prompt_lens[i]), rng)]
@@ -136,6 +142,41 @@ def test_mixed_batch_one_layer_routed():
                                        L.cu_seqlens_q, kv_start, True, c.sm_scale, rows=sample)
     assert_close(o[nd:][sample], pw[sample], what="prefill rows")
     assert_lse_close(ls[nd:][sample], plw[sample])
+    return float(np.abs(o[:nd] - want).max()), float(np.abs(o[nd:][sample] - pw[sample]).max())
+
+
+def test_mixed_batch_one_layer_routed():
+    """Decode rows 0..31 and prefill rows 32.. of one layer land in one output tensor."""
+    step("fullsize mixed batch layer 0: gather -> prefill -> decode")
+    _check_routed_layer(synth.mixed_batch_layer(0), seed=5)
+
+
+N_LAYERS = 36
+
+
+def test_mixed_batch_all_36_layers():
+    """Every layer of the 36-layer mixed batch (seed 5000 + layer), each routed and checked
+    as layer 0 is.  Host input generation takes about a minute per layer, so the layers are
+    generated in worker processes (no GPU use there) a few ahead of the checks; opt in with
+    EKV_ALL_LAYERS=1."""
+    if os.environ.get("EKV_ALL_LAYERS") != "1":
+        pytest.skip("36 layers of host input generation (about a minute each); set EKV_ALL_LAYERS=1")
+    workers = max(1, min(12, (os.cpu_count() or 2) - 2))
+    ahead = workers + 2
+    ctx = multiprocessing.get_context("spawn")
+    worst = [0.0, 0.0]
+    with concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        pending = {li: ex.submit(synth.mixed_batch_layer, li) for li in range(min(N_LAYERS, ahead))}
+        for li in range(N_LAYERS):
+            L = pending.pop(li).result()
+            if li + ahead < N_LAYERS:
+                pending[li + ahead] = ex.submit(synth.mixed_batch_layer, li + ahead)
+            step(f"mixed batch layer {li}: gather -> prefill -> decode")
+            dec_err, pf_err = _check_routed_layer(L, seed=5 + li)
+            worst = [max(worst[0], dec_err), max(worst[1], pf_err)]
+            print(f"layer {li}: decode max-abs {dec_err:.2e}, prefill max-abs {pf_err:.2e}", flush=True)
+            del L
+    print(f"all {N_LAYERS} layers: worst decode max-abs {worst[0]:.2e}, prefill {worst[1]:.2e}", flush=True)
 
 
 def test_writer_quantizes_32x8192_prompts_into_16384_pages():

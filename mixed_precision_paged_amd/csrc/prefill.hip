@@ -69,10 +69,10 @@ struct SmemV {
 };
 
 // V^T column swizzle of the paged source: the 8-byte key quad kq of V^T row
-// d is stored at quad kq ^ ((d / 32) & 3).  There a wavefront stages the four
-// key quads of one page for all 16 d-octets, and the plain layout would put
-// those stores on a quarter of the LDS banks; the swizzle spreads them and
-// keeps the MFMA reads conflict-free.  The workspace source stages sixteen
+// d is stored at quad kq ^ ((d / 32) & 3).  There a wavefront stages the key
+// quads of its pages for every d-octet, and the plain layout would put those
+// stores on a fraction of the LDS banks; the swizzle spreads them and keeps
+// the MFMA reads conflict-free.  The workspace source stages sixteen
 // key quads per wavefront and is faster unswizzled.  The value depends on d / 8
 // only: one per staging thread (rows 8 oc .. 8 oc + 7) and per MFMA read.
 template <bool SWZ>
@@ -609,8 +609,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   };
 
   // Prologue: K(0), V(0), K(1) into LDS, then S(0).  Paged source: a tile's
-  // page metadata is read from LDS when its loads are issued (carrying it
-  // one tile ahead in registers made the head-dim-128 kernel spill).
+  // page metadata is read from LDS when its loads are issued, not carried a
+  // tile ahead in registers.
   issue_k(0, meta(0));
   issue_v(0, meta(0));
   put_k(kbuf[0]);

@@ -124,6 +124,36 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr() or None
 
 
+_F16, _F32, _I32, _U8 = torch.float16, torch.float32, torch.int32, torch.uint8
+
+
+def _arg(t: Optional[torch.Tensor], name: str, dtypes=None) -> Optional[int]:
+    """Device pointer of a contiguous GPU tensor of an expected dtype (None passes through):
+    a host tensor would hand the kernels a host address."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor, got one on {t.device}")
+    if dtypes is not None:
+        dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+        if t.dtype not in dtypes:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+    return _ptr(t)
+
+
+def _same_shape(a: Optional[torch.Tensor], b: Optional[torch.Tensor], what: str) -> None:
+    if a is not None and b is not None and tuple(a.shape) != tuple(b.shape):
+        raise ValueError(f"{what}: shapes {tuple(a.shape)} and {tuple(b.shape)} differ")
+
+
+def _kv_ref(kv: PagedKV):
+    """The descriptor for the call, after checking that its pools live on the GPU."""
+    for t in getattr(kv, "_tensors", ()):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"page pools must be device tensors, got one on {t.device}")
+    return ctypes.byref(kv)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -180,15 +210,17 @@ def ekv_decode_attention(kv: PagedKV, q: torch.Tensor, page_table: torch.Tensor,
                          stream=None) -> None:
     """GQA decode over paged TARGET/compact KV (see ekv.h).  Writes ``out`` (and ``lse``)."""
     batch, hq, _ = q.shape
+    _same_shape(page_table, fidelity, "page_table and fidelity")
     if scratch is None:
         need = ekv_decode_scratch_bytes(batch, hq, kv.num_kv_heads, kv.head_dim, max_seq_len,
                                         pages_per_split)
         scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(_lib.ekv_decode_attention(
-        ctypes.byref(kv), _ptr(q), batch, hq, _ptr(page_table), int(page_table.shape[1]),
-        _ptr(fidelity), _ptr(seq_lens), int(max_seq_len), float(sm_scale), _ptr(out),
-        _dtype_code(out), _ptr(lse), int(pages_per_split), _ptr(scratch),
-        scratch.numel() * scratch.element_size(), _stream(stream)))
+        _kv_ref(kv), _arg(q, "q", _F16), batch, hq, _arg(page_table, "page_table", _I32),
+        int(page_table.shape[1]), _arg(fidelity, "fidelity", _U8), _arg(seq_lens, "seq_lens", _I32),
+        int(max_seq_len), float(sm_scale), _arg(out, "out"), _dtype_code(out), _arg(lse, "lse", _F32),
+        int(pages_per_split), _arg(scratch, "scratch"), scratch.numel() * scratch.element_size(),
+        _stream(stream)))
 
 
 def ekv_decode_attention_elastic(kv: PagedKV, q: torch.Tensor, page_table: torch.Tensor,
@@ -200,25 +232,26 @@ def ekv_decode_attention_elastic(kv: PagedKV, q: torch.Tensor, page_table: torch
     """Decode over TARGET / compact / ElasticKV BASE pages (see ekv.h): per-page flags
     (0, 1, 2) or per-sequence BASE bounds [B, 2] for TARGET-BASE-TARGET layouts."""
     batch, hq, _ = q.shape
+    _same_shape(page_table, fidelity, "page_table and fidelity")
     if scratch is None:
         need = ekv_decode_scratch_bytes(batch, hq, kv.num_kv_heads, kv.head_dim, max_seq_len,
                                         pages_per_split)
         scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(_lib.ekv_decode_attention_elastic(
-        ctypes.byref(kv), _ptr(q), batch, hq, _ptr(page_table), int(page_table.shape[1]),
-        _ptr(fidelity), _ptr(base_bounds), 1 if has_base else 0, _ptr(seq_lens), int(max_seq_len),
-        float(sm_scale), _ptr(out), _dtype_code(out), _ptr(lse), int(pages_per_split), _ptr(scratch),
-        scratch.numel() * scratch.element_size(), _stream(stream)))
+        _kv_ref(kv), _arg(q, "q", _F16), batch, hq, _arg(page_table, "page_table", _I32),
+        int(page_table.shape[1]), _arg(fidelity, "fidelity", _U8), _arg(base_bounds, "base_bounds", _I32),
+        1 if has_base else 0, _arg(seq_lens, "seq_lens", _I32), int(max_seq_len), float(sm_scale),
+        _arg(out, "out"), _dtype_code(out), _arg(lse, "lse", _F32), int(pages_per_split),
+        _arg(scratch, "scratch"), scratch.numel() * scratch.element_size(), _stream(stream)))
 
 
 def ekv_pack_base_pairs(kv: PagedKV, src_a: torch.Tensor, src_b: torch.Tensor, dst: torch.Tensor,
                         stream=None) -> None:
     """Pack TARGET block pairs into BASE blocks in the TARGET pools (see ekv.h)."""
-    for t in (src_a, src_b, dst):
-        if t.dtype != torch.int32:
-            raise TypeError("src_a, src_b and dst must be int32")
-    _check(_lib.ekv_pack_base_pairs(ctypes.byref(kv), _ptr(src_a), _ptr(src_b), _ptr(dst),
-                                    int(dst.shape[0]), _stream(stream)))
+    _same_shape(src_a, dst, "src_a and dst")
+    _same_shape(src_b, dst, "src_b and dst")
+    _check(_lib.ekv_pack_base_pairs(_kv_ref(kv), _arg(src_a, "src_a", _I32), _arg(src_b, "src_b", _I32),
+                                    _arg(dst, "dst", _I32), int(dst.shape[0]), _stream(stream)))
 
 
 def ekv_gather_compact_pages(kv: PagedKV, page_ids: torch.Tensor, apply_scale: bool,
@@ -226,9 +259,12 @@ def ekv_gather_compact_pages(kv: PagedKV, page_ids: torch.Tensor, apply_scale: b
                              stream=None) -> None:
     """Gather compact pages into the FP16 workspace (see ekv.h)."""
     n = int(page_ids.shape[0]) if n_pages is None else int(n_pages)
+    if n > int(page_ids.shape[0]):
+        raise ValueError(f"n_pages {n} exceeds the {int(page_ids.shape[0])} page ids given")
+    _same_shape(ws_k, ws_v, "ws_k and ws_v")
     _check(_lib.ekv_gather_compact_pages(
-        ctypes.byref(kv), _ptr(page_ids), n, 1 if apply_scale else 0, _ptr(ws_k), _ptr(ws_v),
-        int(ws_k.shape[0]), _stream(stream)))
+        _kv_ref(kv), _arg(page_ids, "page_ids", _I32), n, 1 if apply_scale else 0,
+        _arg(ws_k, "ws_k", _F16), _arg(ws_v, "ws_v", _F16), int(ws_k.shape[0]), _stream(stream)))
 
 
 def ekv_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -240,11 +276,15 @@ def ekv_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     q: [T, Hq, D]; k, v: [R, Hkv, D] (or the workspace view [pages, 16, Hkv, D])."""
     q_rows, hq, d = q.shape
     hkv = int(k.shape[-2])
+    if int(k.shape[-1]) != d:
+        raise ValueError(f"K rows have head dim {int(k.shape[-1])}, queries {d}")
+    _same_shape(k, v, "k and v")
     kv_rows = k.numel() // (hkv * d)
     _check(_lib.ekv_prefill_attention(
-        _ptr(q), q_rows, _ptr(k), _ptr(v), kv_rows, _ptr(cu_seqlens_q), _ptr(kv_start),
+        _arg(q, "q", _F16), q_rows, _arg(k, "k", _F16), _arg(v, "v", _F16), kv_rows,
+        _arg(cu_seqlens_q, "cu_seqlens_q", _I32), _arg(kv_start, "kv_start", _I32),
         int(kv_start.shape[0]), int(max_len), hq, hkv, d, 1 if causal else 0, float(sm_scale),
-        _ptr(out), _dtype_code(out), _ptr(lse), _stream(stream)))
+        _arg(out, "out"), _dtype_code(out), _arg(lse, "lse", _F32), _stream(stream)))
 
 
 def ekv_prefill_paged_attention(kv: PagedKV, q: torch.Tensor, cu_seqlens_q: torch.Tensor,
@@ -255,23 +295,24 @@ def ekv_prefill_paged_attention(kv: PagedKV, q: torch.Tensor, cu_seqlens_q: torc
 
     q: [T, Hq, D]; page_table: [n_prompts, stride] int32; fidelity: same shape uint8 or None."""
     q_rows, hq, _ = q.shape
+    _same_shape(page_table, fidelity, "page_table and fidelity")
     _check(_lib.ekv_prefill_paged_attention(
-        ctypes.byref(kv), _ptr(q), q_rows, _ptr(cu_seqlens_q), _ptr(page_table),
-        int(page_table.shape[1]), _ptr(fidelity), int(page_table.shape[0]), int(max_len), hq,
-        1 if causal else 0, float(sm_scale), _ptr(out), _dtype_code(out), _ptr(lse), _stream(stream)))
+        _kv_ref(kv), _arg(q, "q", _F16), q_rows, _arg(cu_seqlens_q, "cu_seqlens_q", _I32),
+        _arg(page_table, "page_table", _I32), int(page_table.shape[1]), _arg(fidelity, "fidelity", _U8),
+        int(page_table.shape[0]), int(max_len), hq, 1 if causal else 0, float(sm_scale),
+        _arg(out, "out"), _dtype_code(out), _arg(lse, "lse", _F32), _stream(stream)))
 
 
 def ekv_append_tokens(kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor,
                       slot_mapping: torch.Tensor, stream=None) -> None:
     """Write new tokens' K/V rows ([n, Hkv, D] fp16) into TARGET slots (see ekv.h).
     ``kv`` must describe writable TARGET pools."""
-    for t in (k_new, v_new):
-        if t.dtype != torch.float16:
-            raise TypeError(f"new K/V rows have dtype {t.dtype}, expected float16")
-    if slot_mapping.dtype != torch.int32:
-        raise TypeError("slot_mapping must be int32")
-    _check(_lib.ekv_append_tokens(ctypes.byref(kv), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
-                                  int(slot_mapping.shape[0]), _stream(stream)))
+    _same_shape(k_new, v_new, "k_new and v_new")
+    if k_new.numel() != int(slot_mapping.shape[0]) * kv.num_kv_heads * kv.head_dim:
+        raise ValueError("k_new/v_new must hold one [Hkv, D] row per slot_mapping entry")
+    _check(_lib.ekv_append_tokens(_kv_ref(kv), _arg(k_new, "k_new", _F16), _arg(v_new, "v_new", _F16),
+                                  _arg(slot_mapping, "slot_mapping", _I32), int(slot_mapping.shape[0]),
+                                  _stream(stream)))
 
 
 def ekv_quantize_pages(kv: PagedKV, k_src: torch.Tensor, v_src: torch.Tensor,
@@ -281,18 +322,19 @@ def ekv_quantize_pages(kv: PagedKV, k_src: torch.Tensor, v_src: torch.Tensor,
 
     k_src, v_src: [rows, Hkv, D] (or the TARGET pool view [pages, 16, Hkv, D]).
     ``kv`` must describe writable compact pools."""
-    for t in (k_src, v_src):
-        if t.dtype != torch.float16:
-            raise TypeError(f"source rows have dtype {t.dtype}, expected float16")
-    for t in (src_row_start, dst_pages, n_valid):
-        if t is not None and t.dtype != torch.int32:
-            raise TypeError("src_row_start, dst_pages and n_valid must be int32")
+    _same_shape(k_src, v_src, "k_src and v_src")
+    _same_shape(src_row_start, dst_pages, "src_row_start and dst_pages")
+    _same_shape(n_valid, dst_pages, "n_valid and dst_pages")
     rows = k_src.numel() // (kv.num_kv_heads * kv.head_dim)
-    _check(_lib.ekv_quantize_pages(ctypes.byref(kv), _ptr(k_src), _ptr(v_src), rows,
-                                   _ptr(src_row_start), _ptr(n_valid), _ptr(dst_pages),
+    _check(_lib.ekv_quantize_pages(_kv_ref(kv), _arg(k_src, "k_src", _F16), _arg(v_src, "v_src", _F16),
+                                   rows, _arg(src_row_start, "src_row_start", _I32),
+                                   _arg(n_valid, "n_valid", _I32), _arg(dst_pages, "dst_pages", _I32),
                                    int(dst_pages.shape[0]), _stream(stream)))
 
 
 def ekv_e4m3_to_f16(codes: torch.Tensor, out: torch.Tensor, method: int, stream=None) -> None:
     """Diagnostic: device E4M3 -> fp16 conversion (0 = decode path, 1 = gather path)."""
-    _check(_lib.ekv_e4m3_to_f16(_ptr(codes), int(codes.numel()), _ptr(out), int(method), _stream(stream)))
+    if out.numel() != codes.numel():
+        raise ValueError("out must hold one fp16 value per code")
+    _check(_lib.ekv_e4m3_to_f16(_arg(codes, "codes", _U8), int(codes.numel()), _arg(out, "out", _F16),
+                                int(method), _stream(stream)))

@@ -236,3 +236,35 @@ def test_descriptor_keeps_its_tensors_alive():
     del t
     gc.collect()
     assert ref() is not None and kv._tensors[0] is ref()
+
+
+def test_binding_rejects_host_tensors_and_bad_shapes():
+    """The Python binding refuses, before any library call, tensors that would hand the
+    kernels host addresses, and shape pairs the entry points assume equal."""
+    import torch
+
+    kv = ekv.paged_kv(8, 128, k_compact=torch.zeros((4, 16, 8, 128), dtype=torch.float16),
+                      v_compact=torch.zeros((4, 16, 8, 128), dtype=torch.uint8),
+                      v_scale=torch.ones((4, 8), dtype=torch.float32))
+    q = torch.zeros((1, 32, 128), dtype=torch.float16)
+    pt = torch.zeros((1, 4), dtype=torch.int32)
+    lens = torch.full((1,), 64, dtype=torch.int32)
+    out = torch.zeros((1, 32, 128), dtype=torch.float32)
+    with pytest.raises(ValueError, match="device"):
+        ekv.ekv_decode_attention(kv, q, pt, None, lens, 64, 0.088, out)
+    with pytest.raises(ValueError, match="device"):
+        ekv.ekv_prefill_attention(q, torch.zeros((16, 8, 128), dtype=torch.float16),
+                                  torch.zeros((16, 8, 128), dtype=torch.float16),
+                                  torch.zeros(2, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                                  1, 0.088, out)
+    with pytest.raises(ValueError, match="differ"):
+        ekv.ekv_prefill_attention(q, torch.zeros((16, 8, 128), dtype=torch.float16),
+                                  torch.zeros((8, 8, 128), dtype=torch.float16),
+                                  torch.zeros(2, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                                  1, 0.088, out)
+    ids = torch.zeros(2, dtype=torch.int32)
+    ws = torch.zeros((4, 16, 8, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="exceeds"):
+        ekv.ekv_gather_compact_pages(kv, ids, True, ws, ws, n_pages=3)
+    with pytest.raises(ValueError, match="differ"):
+        ekv.ekv_decode_attention(kv, q, pt, torch.zeros((1, 5), dtype=torch.uint8), lens, 64, 0.088, out)

@@ -26,7 +26,9 @@ def test_tiny_decode_case():
     np.testing.assert_array_equal(out_nf, out32)
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 128), (16, 8, 64), (4, 2, 64), (8, 1, 128)])
+# every (head dim, query heads per KV head) kernel instantiation: D 64 / 128 x G 1, 2, 4, 8
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 128), (16, 8, 128), (8, 1, 128),
+                                      (8, 8, 64), (16, 8, 64), (8, 2, 64), (16, 2, 64)])
 def test_mixed_fidelity_ragged(hq, hkv, d):
     step(f"decode mixed hq={hq} hkv={hkv} d={d}")
     c = synth.make_paged_case(100 + hq + d, LENS, hq, hkv, d, compact_frac=0.3,

@@ -68,7 +68,7 @@ def test_split_count_does_not_change_the_result():
         assert max_abs(o, outs[0]) <= TOL
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 2, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 2, 64), (8, 8, 128), (16, 2, 64), (16, 8, 64)])
 def test_balanced_plan_ragged_empty_and_bad(hq, hkv, d):
     """Equal page-head shares per workgroup: sequences held whole by one range (1-page
     ones), cut over a few ranges and spread over hundreds (few page-heads, 512

@@ -623,6 +623,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   f32x16 sA[2], sB[2];
   qk_block(sA[0], kbuf[0], 0);
   qk_block(sA[1], kbuf[0], 1);
+  // The first iteration stores K(2) into buffer 0: every wavefront must have
+  // read K(0) from it first (later reuses are ordered by the per-tile barrier).
+  __syncthreads();
 
   // Iteration t: loads of K(t+2) and V(t+1) are in flight while S(t+1) is
   // computed on the matrix cores and the softmax of S(t) runs on the vector
@@ -963,6 +966,9 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
   f32x16 sA[2], sB[2];
   qk_block(sA[0], 0, 0);
   qk_block(sA[1], 0, 1);
+  // The first iteration stages K(2) into buffer 0: every wavefront must have
+  // read K(0) from it first (later reuses are ordered by the per-tile barrier).
+  __syncthreads();
 
   // Iteration t: K(t+2) and V(t+1) stream into LDS while S(t+1) runs on the
   // matrix cores and the softmax of S(t) on the vector ALUs, then O += V(t)

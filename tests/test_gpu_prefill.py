@@ -139,3 +139,36 @@ def test_prefill_row_equals_decode_over_prefix():
         od, ld = dc.decode(torch.float32, q=q, rows=[0], seq_lens=lens, max_seq_len=77)
         assert max_abs(out[i], od[0]) <= tol
         assert abs(float(lse[i, 0]) - float(ld[0, 0])) <= 2 * TOL
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(128, 32, 8), (64, 16, 2)])
+def test_repeat_launches_give_identical_bits(d, hq, hkv):
+    """Both prefill kernels, both sources (workspace and pages), launched repeatedly on the
+    same inputs give the same bits: every LDS tile reuse is ordered by a barrier (including
+    the first, where tile 2's keys land in the buffer tile 0's keys were read from)."""
+    step(f"prefill repeat launches d={d}")
+    pc = synth.make_prefill_case(91 + d, [700, 1029, 64, 333], hq, hkv, d)
+    c = pc.paged
+    dc = DeviceCase(c)
+    prompts = list(range(len(pc.prompt_lens)))
+    ids, kv_start = pc.chunk_pages(prompts)
+    ws_k = torch.empty((len(ids), 16, hkv, d), dtype=torch.float16, device="cuda")
+    ws_v = torch.empty_like(ws_k)
+    ekv().ekv_gather_compact_pages(dc.kv(), dev(ids), True, ws_k, ws_v)
+    q = dev(c.q)
+    cu = dev(pc.cu_seqlens_q)
+    L = int(pc.prompt_lens.max())
+    first = {}
+    for rep in range(6):
+        for route in ("ws", "paged"):
+            out = torch.empty((q.shape[0], hq, d), dtype=torch.float32, device="cuda")
+            if route == "ws":
+                ekv().ekv_prefill_attention(q, ws_k, ws_v, cu, dev(kv_start), L, c.sm_scale, out)
+            else:
+                ekv().ekv_prefill_paged_attention(dc.kv(), q, cu, dc.page_table, None, L, c.sm_scale, out)
+            torch.cuda.synchronize()
+            if rep == 0:
+                first[route] = out
+            else:
+                assert torch.equal(out.view(torch.int32), first[route].view(torch.int32)), (route, rep)
+    assert torch.equal(first["ws"].view(torch.int32), first["paged"].view(torch.int32))

@@ -73,6 +73,11 @@ def calibrate_copy():
 
 def main():
     args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every workload runs on a single MI355X.  Sequences and "
+              "KV heads would shard across GPUs with no exchange inside attention; that is not "
+              "implemented.", file=sys.stderr)
+        sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
         return
@@ -88,11 +93,6 @@ def main():
     if args.workload == "elastic":
         bench_elastic(args)
         return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the decode hot path on a single MI355X "
-              "(sequences and KV heads shard across GPUs with no exchange; not built here).",
-              file=sys.stderr)
-        sys.exit(2)
 
     import torch
 

@@ -268,3 +268,16 @@ def test_binding_rejects_host_tensors_and_bad_shapes():
         ekv.ekv_gather_compact_pages(kv, ids, True, ws, ws, n_pages=3)
     with pytest.raises(ValueError, match="differ"):
         ekv.ekv_decode_attention(kv, q, pt, torch.zeros((1, 5), dtype=torch.uint8), lens, 64, 0.088, out)
+
+
+@pytest.mark.parametrize("workload", ["decode", "prefill", "mixed", "writer", "elastic"])
+def test_bench_refuses_more_than_one_gpu(workload):
+    """bench.py runs on one GPU only; asking for more exits with status 2 and says why,
+    before touching any device."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", "--workload", workload],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

@@ -21,9 +21,9 @@
 // S^T register layout, and V^T is read in the same order.  S of tile t + 1 is
 // computed in the same instruction stream as the softmax of tile t.
 // Launch order: workgroups are mapped so that each XCD (8 per MI355X, each
-// with its own L2) walks a contiguous range of (prompt, head, row tile), so
-// the K/V rows a head reuses stay in one L2; within a head the longest
-// (last) causal row tiles start first.
+// with its own L2) walks a contiguous range of (prompt, KV head) groups, so
+// the K/V rows the group's query heads share stay in one L2; within a group
+// the longest (last) causal row tiles of all its query heads start first.
 //
 // Two kernels, one arithmetic (identical operands and order, so their outputs
 // agree bit for bit).  Sources: the gather workspace, or the direct route over
@@ -339,6 +339,31 @@ __device__ void write_nan_rows(const PrefillParams& p, int64_t q0, int r_lo, int
   }
 }
 
+// Work item of this workgroup: (prompt, query head, row tile).  Each XCD (own
+// L2) takes a contiguous range of items, and within it the items are grouped
+// by (prompt, KV head): the G query heads that read the same K/V rows run
+// together.  Inside a group the row tiles go longest first across all G
+// heads (a causal row tile's work grows with its index), so the long tiles
+// start first and the short ones fill the end; ordering only within each
+// head leaves a sawtooth of long tiles late in the range (about a fifth
+// longer runs for 2048-token prompts in a list-schedule model).
+struct WorkItem {
+  int prompt, h, mt;
+};
+__device__ __forceinline__ WorkItem work_item(const PrefillParams& p, int n_mtiles) {
+  const int total = (int)gridDim.x;
+  const int bid = blockIdx.x;
+  const int work = (total % kXcds == 0) ? (bid % kXcds) * (total / kXcds) + bid / kXcds : bid;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int per_group = G * n_mtiles;
+  const int grp = work / per_group, r = work % per_group;
+  WorkItem wi;
+  wi.mt = n_mtiles - 1 - r / G;
+  wi.h = (grp % p.num_kv_heads) * G + r % G;
+  wi.prompt = grp / p.num_kv_heads;
+  return wi;
+}
+
 // Paged source: stages the prompt's page ids, kinds and scales of pages
 // 0 .. n_pages - 1 in LDS (meta = (phys << 1) | kind; scale 1 for a TARGET
 // page).  Pages past the prompt get a copy of page 0, which is in bounds:
@@ -393,13 +418,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   __shared__ int s_bad;
 
   // XCD-aware work mapping (see header).
-  const int total = (int)(gridDim.x);
-  const int bid = blockIdx.x;
-  const int work = (total % kXcds == 0) ? (bid % kXcds) * (total / kXcds) + bid / kXcds : bid;
-  const int mt_rev = work % n_mtiles;
-  const int h = (work / n_mtiles) % p.num_q_heads;
-  const int prompt = work / (n_mtiles * p.num_q_heads);
-  const int mt = n_mtiles - 1 - mt_rev;
+  const WorkItem wi = work_item(p, n_mtiles);
+  const int prompt = wi.prompt, h = wi.h, mt = wi.mt;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int g = h / G;
 
@@ -728,13 +748,8 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
   __shared__ int s_bad;
 
   // XCD-aware work mapping (as in prefill_kernel).
-  const int total = (int)(gridDim.x);
-  const int bid = blockIdx.x;
-  const int work = (total % kXcds == 0) ? (bid % kXcds) * (total / kXcds) + bid / kXcds : bid;
-  const int mt_rev = work % n_mtiles;
-  const int h = (work / n_mtiles) % p.num_q_heads;
-  const int prompt = work / (n_mtiles * p.num_q_heads);
-  const int mt = n_mtiles - 1 - mt_rev;
+  const WorkItem wi = work_item(p, n_mtiles);
+  const int prompt = wi.prompt, h = wi.h, mt = wi.mt;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int g = h / G;
 

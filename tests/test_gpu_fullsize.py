@@ -99,35 +99,49 @@ def test_compact_prefill_32x8192_in_four_chunks():
         del out, lse, q
 
 
-def _check_routed_layer(L, seed):
-    """Route one mixed-batch layer into one output tensor (gather -> prefill into rows
-    n_decode.., then decode into rows 0..n_decode-1) and check it against the oracle:
-    every decode row, sampled prefill rows, and every row written by its own path."""
+def _route_layer(L, dc, two_streams=False):
+    """Route one mixed-batch layer into one output tensor: gather -> prefill into rows
+    n_decode.. (workspace reused per layer), and decode into rows 0..n_decode-1 -- on the
+    same stream, or on a second stream beside the gather + prefill."""
     c = L.paged
-    dc = DeviceCase(c)
     H, D, Hq = c.num_kv_heads, c.head_dim, c.num_q_heads
     nd = L.n_decode
     T = int(L.cu_seqlens_q[-1])
     out = torch.full((nd + T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((nd + T, Hq), float("nan"), dtype=torch.float32, device="cuda")
-    # prefill route first (workspace reused per layer), then decode
     prompts = list(range(nd, nd + len(L.prompt_lens)))
     ids = np.concatenate([c.page_table[p, :(int(c.seq_lens[p]) + 15) // 16] for p in prompts]).astype(np.int32)
     kv_start = np.concatenate([[0], np.cumsum((L.prompt_lens + 15) // 16 * 16)[:-1]]).astype(np.int32)
     ws_k = torch.empty((4096, 16, H, D), dtype=torch.float16, device="cuda")
     ws_v = torch.empty_like(ws_k)
-    ekv().ekv_gather_compact_pages(dc.kv(), dev(ids), True, ws_k, ws_v)
-    ekv().ekv_prefill_attention(dev(L.q_prefill), ws_k, ws_v, dev(L.cu_seqlens_q), dev(kv_start),
-                                int(L.prompt_lens.max()), c.sm_scale, out[nd:], lse[nd:])
     lens = c.seq_lens[:nd]
     pps = ekv().ekv_decode_plan_pages_per_split(lens, H)
-    ekv().ekv_decode_attention(dc.kv(), dev(L.q_decode), dc.page_table[:nd].contiguous(),
-                               dc.fidelity[:nd].contiguous(), dev(lens), int(lens.max()), c.sm_scale,
-                               out[:nd], lse[:nd], pages_per_split=pps)
+    # every input on the device first, then the launches
+    ids_d, ks_d, qp, cu = dev(ids), dev(kv_start), dev(L.q_prefill), dev(L.cu_seqlens_q)
+    q_dec, lens_d = dev(L.q_decode), dev(lens)
+    pt, fl = dc.page_table[:nd].contiguous(), dc.fidelity[:nd].contiguous()
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream() if two_streams else main
+    side.wait_stream(main)  # the inputs and the output buffers are ready
+    ekv().ekv_gather_compact_pages(dc.kv(), ids_d, True, ws_k, ws_v, stream=main)
+    ekv().ekv_prefill_attention(qp, ws_k, ws_v, cu, ks_d, int(L.prompt_lens.max()), c.sm_scale,
+                                out[nd:], lse[nd:], stream=main)
+    ekv().ekv_decode_attention(dc.kv(), q_dec, pt, fl, lens_d, int(lens.max()), c.sm_scale,
+                               out[:nd], lse[:nd], pages_per_split=pps, stream=side)
     torch.cuda.synchronize()
-    o = out.cpu().numpy()
-    ls = lse.cpu().numpy()
-    del out, lse, ws_k, ws_v, dc
+    return out.cpu().numpy(), lse.cpu().numpy(), ids, kv_start
+
+
+def _check_routed_layer(L, seed, dc=None):
+    """Route one mixed-batch layer and check it against the oracle: every decode row,
+    sampled prefill rows, and every row written by its own path."""
+    c = L.paged
+    dc = DeviceCase(c) if dc is None else dc
+    H, D = c.num_kv_heads, c.head_dim
+    nd = L.n_decode
+    lens = c.seq_lens[:nd]
+    prompts = list(range(nd, nd + len(L.prompt_lens)))
+    o, ls, ids, kv_start = _route_layer(L, dc)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(ls)), "every row written by its own path"
     want, wlse = oracle.decode_attention(L.q_decode, c.k_target, c.v_target, c.k_compact, c.v_compact,
                                          c.v_scale, c.page_table[:nd], c.fidelity[:nd], lens, c.sm_scale)
@@ -146,9 +160,17 @@ def _check_routed_layer(L, seed):
 
 
 def test_mixed_batch_one_layer_routed():
-    """Decode rows 0..31 and prefill rows 32.. of one layer land in one output tensor."""
+    """Decode rows 0..31 and prefill rows 32.. of one layer land in one output tensor; with
+    the decode on a second stream beside the gather + prefill the output is the same bits."""
     step("fullsize mixed batch layer 0: gather -> prefill -> decode")
-    _check_routed_layer(synth.mixed_batch_layer(0), seed=5)
+    L = synth.mixed_batch_layer(0)
+    dc = DeviceCase(L.paged)
+    _check_routed_layer(L, seed=5, dc=dc)
+    step("fullsize mixed batch layer 0: decode on a second stream")
+    o1, l1, _, _ = _route_layer(L, dc)
+    o2, l2, _, _ = _route_layer(L, dc, two_streams=True)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
 
 
 N_LAYERS = 36

@@ -34,6 +34,14 @@
 //   (max, sum, unnormalized acc) partials and the merge kernel combines them:
 //   M = max m_s, L = sum l_s 2^(m_s-M), o = sum acc_s 2^(m_s-M) / L,
 //   lse = (M + log2 L) ln 2.
+//   Ragged batches (balanced plan): every workgroup takes an equal,
+//   contiguous share of the batch's page-heads in (sequence, KV head, page)
+//   order, found by a binary search over prefix sums of the page counts; a
+//   share may cut (sequence, head) ranges at either end and span several, and
+//   each range it holds runs through the same page loop.  A range that is a
+//   whole (sequence, head) is written directly, the rest go through the
+//   merge, which finds a cut range's pieces in the workgroups its share
+//   spans.
 #include "ekv_device.hpp"
 #include "ekv_internal.hpp"
 

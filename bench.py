@@ -578,22 +578,36 @@ def bench_elastic(args):
 
 def counted_traffic(pps):
     """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, or None when the decode kernel sources or the split plan changed since
-    it was taken."""
-    import hashlib
+    summary, or None when the decode kernel code or the split plan changed since it
+    was taken."""
     import re
 
     path = os.path.join(ROOT, "profiles", "decode_compact_b32_ctx8192_pmc.md")
-    srcs = [os.path.join(ROOT, "mixed_precision_paged_amd", "csrc", f)
-            for f in ("decode.hip", "ekv_device.hpp", "ekv_internal.hpp")]
     try:
         text = open(path).read()
         rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
-        h = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()
+        h = decode_code_hash()
     except (OSError, AttributeError, ValueError):
         return None
-    same = rec.get("kernel_sources_sha256") == h and rec.get("pages_per_split") == pps
+    same = rec.get("kernel_code_sha256") == h and rec.get("pages_per_split") == pps
     return int(rec["traffic_bytes_per_call"]) if same else None
+
+
+def decode_code_hash():
+    """sha256 of the decode kernel's sources with comments and whitespace removed: it
+    changes when the compiled code can, not when a comment does."""
+    import hashlib
+    import re
+
+    srcs = [os.path.join(ROOT, "mixed_precision_paged_amd", "csrc", f)
+            for f in ("decode.hip", "ekv_device.hpp", "ekv_internal.hpp")]
+    code = []
+    for f in srcs:
+        t = open(f).read()
+        t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        code.append(" ".join(t.split()))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()
 
 
 def cpu_baseline(case, algo_bytes, min_seconds):

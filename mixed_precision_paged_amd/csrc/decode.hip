@@ -726,7 +726,6 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeParams p) {
         L += p.part_ml[k * 2 + 1] * f_lane;
       }
       const int cnt = min(kWave, nsplit - s0);
-#pragma unroll 4
       for (int j = 0; j < cnt; ++j) {
         const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f_lane), j));
         const int64_t k = rec(s0 + j);

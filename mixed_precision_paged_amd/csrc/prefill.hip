@@ -707,7 +707,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
 //   Staging: each wavefront moves 4 K and 4 V row quads (1 KiB each) per
 //   tile; lane l writes bytes 16 l of its quad, i.e. row l / 16, swizzled
 //   chunk l % 16, so it loads the source chunk that belongs there.  Rows past
-//   the prompt are outside the descriptor range and arrive as zeros.
+//   the prompt are outside the descriptor range and arrive as zeros (paged
+//   source: value rows; its key rows past the prompt are masked instead).
 //   V^T operand: ds_read_b64_tr_b16 returns, in lane j of each 16-lane group,
 //   element j % 4 of the 8-byte pieces addressed by lanes 4k + j / 4 (k =
 //   0..3); lane i of the group addresses key row key0 + i / 4 at d offset

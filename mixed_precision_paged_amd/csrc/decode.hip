@@ -52,9 +52,9 @@ constexpr float kTau = 8.0f;          // deferred-rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;   // "no token yet" running max
 constexpr bool kHeadMajorGrid = true; // launch order: the KV heads of one (sequence, split) adjacent
 constexpr int kMaxSplitPages = 512;   // pages per split (metadata staged in LDS)
-constexpr int kBalancedRound = 512;     // balanced plan: workgroups per round (2 per CU)
-constexpr int kBalancedMaxPages = 512;  // balanced plan: pages per range (LDS stage); measured
-                                        // better than one round of up to 1,024-page ranges
+constexpr int kBalancedRound = 256;     // balanced plan: workgroups per round (one per CU)
+constexpr int kBalancedMaxPages = 512;  // balanced plan: pages per range (LDS stage)
+constexpr int kBalancedWaves = 8;       // balanced plan: wavefronts per workgroup
 constexpr int kSlots = 2;             // register page buffers per wavefront (pages in flight + 1)
 constexpr int kMinWaves = 2;          // occupancy bound (wavefronts per SIMD) for G*D < 1024
 
@@ -579,8 +579,8 @@ __device__ __forceinline__ int wg_of(int64_t x, int64_t W, int n) { return (int)
 __device__ __forceinline__ int64_t wg_start(int i, int64_t W, int n) { return (int64_t)i * W / n; }
 
 template <int D, int G, int MODE>
-__global__ __launch_bounds__(4 * kWave, 2) void decode_balanced_kernel(DecodeParams p) {
-  constexpr int NW = 4;
+__global__ __launch_bounds__(kBalancedWaves * kWave, kMinWaves) void decode_balanced_kernel(DecodeParams p) {
+  constexpr int NW = kBalancedWaves;
   __shared__ PieceSmem<D, G, NW, kBalancedMaxPages> sm;
   __shared__ int s_pref[kDecodeMaxBalancedBatch + 1];  // exclusive prefix sums of page counts
   const int lane = threadIdx.x & (kWave - 1);
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(4 * kWave, 2) void decode_balanced_kernel(DecodePar
   const int64_t w0 = wg_start(i, W, n), w1 = wg_start(i + 1, W, n);
   if (w0 == w1) {  // empty range (fewer page-heads than workgroups): a neutral head record,
     // since the merge reads the head slots of every workgroup a cut sequence spans
-    for (int e = threadIdx.x; e < G * D; e += 4 * kWave) {
+    for (int e = threadIdx.x; e < G * D; e += NW * kWave) {
       p.part_acc[2 * (int64_t)i * G * D + e] = 0.f;
       if (e < G) {
         p.part_ml[(2 * (int64_t)i * G + e) * 2 + 0] = kNegBig;
@@ -774,7 +774,7 @@ hipError_t launch_split(const DecodeParams& p, dim3 grid, hipStream_t stream) {
 template <int D, int G>
 hipError_t launch_balanced(const DecodeParams& p, hipStream_t stream) {
   const int mode = p.has_base ? (p.fidelity ? 2 : 3) : (p.fidelity ? 1 : 0);
-  const dim3 grid(p.n_wg), block(4 * kWave);
+  const dim3 grid(p.n_wg), block(kBalancedWaves * kWave);
   switch (mode) {
     case 0: hipLaunchKernelGGL((decode_balanced_kernel<D, G, 0>), grid, block, 0, stream, p); break;
     case 1: hipLaunchKernelGGL((decode_balanced_kernel<D, G, 1>), grid, block, 0, stream, p); break;
@@ -846,9 +846,10 @@ size_t decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_h
 }
 
 int32_t decode_balanced_workgroups(int32_t batch, int32_t num_kv_heads, int32_t max_pages) {
-  // one round: 2 four-wavefront workgroups per CU on the 256-CU part (the
-  // kernel holds 2 wavefronts per SIMD), more (whole rounds) when a range
-  // would exceed the LDS page-metadata stage
+  // one round: one 8-wavefront workgroup per CU on the 256-CU part (2
+  // wavefronts per SIMD; measured 1% ahead of two 4-wavefront workgroups
+  // per CU), more (whole rounds) when a range would exceed the LDS
+  // page-metadata stage
   const int64_t work = (int64_t)batch * num_kv_heads * max_pages;
   int64_t n = kBalancedRound;
   while ((work + n - 1) / n > kBalancedMaxPages) n += kBalancedRound;

@@ -93,7 +93,7 @@ def test_split_plan_and_scratch_size():
     assert ekv.ekv_decode_pages_per_split(16, 8, 8192) == 128
     # 512 groups: one split each
     assert ekv.ekv_decode_pages_per_split(64, 8, 8192) == 512
-    # balanced plan: 512 workgroups (2 per CU) x 2 partial records of G x (D + 2) floats
+    # balanced plan: 512 workgroups (two rounds of 256) x 2 partial records of G x (D + 2) floats
     bal = ekv.ekv_decode_scratch_bytes(64, 32, 8, 128, 8192, ekv.DECODE_BALANCED)
     recs = 512 * 2 * 4
     assert bal == ((recs * 128 * 4 + 255) // 256) * 256 + recs * 2 * 4

@@ -71,7 +71,7 @@ def test_split_count_does_not_change_the_result():
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 2, 64), (8, 8, 128), (16, 2, 64), (16, 8, 64)])
 def test_balanced_plan_ragged_empty_and_bad(hq, hkv, d):
     """Equal page-head shares per workgroup: sequences held whole by one range (1-page
-    ones), cut over a few ranges and spread over hundreds (few page-heads, 512
+    ones), cut over a few ranges and spread over hundreds (few page-heads, 256
     workgroups), empty ones, and a bad page id that must turn only its rows NaN."""
     step(f"decode balanced plan hq={hq} hkv={hkv} d={d}")
     lens = [1, 5, 16, 0, 17, 300, 2053, 40, 0, 1000, 3, 129, 64, 16, 777, 2]
@@ -86,7 +86,7 @@ def test_balanced_plan_ragged_empty_and_bad(hq, hkv, d):
     assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))
     out16, _ = dc.decode(torch.float16, pages_per_split=ekv().DECODE_BALANCED)
     assert f16_bits_equal_rne(out16, out)
-    # a short batch: 37 + 1 tokens spread over 512 workgroups
+    # a short batch: 37 + 1 tokens spread over 256 workgroups
     c2 = synth.make_paged_case(310 + d, [37, 1], hq, hkv, d, compact_frac=0.5)
     out2, lse2 = DeviceCase(c2).decode(torch.float32, pages_per_split=ekv().DECODE_BALANCED)
     w2, wl2 = oracle_decode(c2)

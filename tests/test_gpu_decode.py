@@ -213,3 +213,20 @@ def test_planted_oracle_mistakes_are_detected():
     pt2[0, targ0[0]], fl2[0, targ0[0]] = c.page_table[1, comp1[0]], 1   # one flag flipped
     for kwargs in (dict(v_scale=sc), dict(page_table=pt), dict(page_table=pt2, fidelity=fl2)):
         assert max_abs(out, oracle_decode(c, **kwargs)[0]) > TOL, list(kwargs)
+
+
+def test_balanced_plan_at_its_batch_limit():
+    """2,048 sequences (the balanced plan's largest batch: the page-count scan runs 32
+    sequences per lane) of 0..300 tokens, mixed fidelity, 8 q / 2 KV heads, head dim 64;
+    the automatic plan picks the balanced one for such a ragged batch."""
+    step("decode balanced plan, 2048 sequences")
+    lens = np.random.default_rng(2048).integers(0, 301, size=2048)
+    assert ekv().ekv_decode_plan_pages_per_split(lens, 2) == ekv().DECODE_BALANCED
+    c = synth.make_paged_case(2048, lens, 8, 2, 64, compact_frac=0.3)
+    dc = DeviceCase(c)
+    want, wlse = oracle_decode(c)
+    out, lse = dc.decode(torch.float32, pages_per_split=ekv().DECODE_BALANCED)
+    assert_close(out, want)
+    assert_lse_close(lse, wlse)
+    empty = lens == 0
+    assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))

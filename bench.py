@@ -52,6 +52,8 @@ def parse():
                          "TARGET append); elastic: ElasticKV BASE decode (structured and general "
                          "paths) and the demotion pack")
     ap.add_argument("--layers", type=int, default=36, help="mixed workload: layers per step")
+    ap.add_argument("--streams", choices=("1", "both"), default="both",
+                    help="mixed workload: time the one-stream routing only, or also the two-stream one")
     ap.add_argument("--distinct-layers", type=int, default=4,
                     help="mixed workload: distinct generated layers cycled over the step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -372,7 +374,7 @@ def bench_mixed(args):
         return e0.elapsed_time(e1) / steps
 
     ms = timed(False)
-    ms2 = timed(True)
+    ms2 = timed(True) if args.streams == "both" else None
     dec_bytes = sum(layers[li % len(layers)]["dec_bytes"] for li in range(args.layers))
     line = {
         "metric": "mixed batch step time (36 layers: gather + prefill + mixed-fidelity decode)",
@@ -384,10 +386,11 @@ def bench_mixed(args):
         "tokens_per_s": {"decode": round(nd / (ms * 1e-3), 1),
                          "prefill": round(4 * 2048 / (ms * 1e-3), 1)},
         "decode_bytes_per_step": int(dec_bytes),
-        "two_streams": {"ms": round(ms2, 3), "speedup": round(ms / ms2, 4),
-                        "what": "each layer's decode on a second stream beside its gather + prefill, "
-                                "joined before the next layer"},
     }
+    if ms2 is not None:
+        line["two_streams"] = {"ms": round(ms2, 3), "speedup": round(ms / ms2, 4),
+                               "what": "each layer's decode on a second stream beside its gather + prefill, "
+                                       "joined before the next layer"}
     print(json.dumps(line), flush=True)
 
 

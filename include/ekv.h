@@ -119,7 +119,9 @@ int32_t ekv_decode_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t 
  * memory), for callers whose scheduler knows them: batches of near-equal
  * lengths get one balanced round (one split per sequence and KV head when
  * there are 192..256 or at least 512 such groups, else about 512 split
- * workgroups); ragged batches (up to 2,048 sequences) get
+ * workgroups), except where that plan would launch between one and two
+ * rounds of split workgroups (more than 768, at most 1,536), which get
+ * EKV_DECODE_BALANCED; ragged batches (up to 2,048 sequences) get
  * EKV_DECODE_BALANCED, larger ragged ones small splits.  Pass the result as
  * `pages_per_split`.  Pure host function; NULL or empty input returns 16.
  */

@@ -66,6 +66,10 @@ ekv_status check_kv(const ekv_paged_kv* kv, bool need_target, bool need_compact)
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
+// 4-wavefront split-plan decode workgroups resident at once on the 256-CU
+// part (3 per CU at their register use).
+constexpr int64_t kSplitRound = 768;
+
 }  // namespace
 
 extern "C" {
@@ -101,8 +105,20 @@ int32_t ekv_decode_plan_pages_per_split(const int32_t* seq_lens_host, int32_t ba
     maxp = n > maxp ? n : maxp;
   }
   if (maxp == 0) return 16;
-  if (total * 10 >= maxp * batch * 9)  // lengths within ~10% of the longest: one balanced round
-    return ekv::decode_auto_pages_per_split(batch, num_kv_heads, (int32_t)maxp);
+  if (total * 10 >= maxp * batch * 9) {  // lengths within ~10% of the longest: splits
+    const int32_t pps = ekv::decode_auto_pages_per_split(batch, num_kv_heads, (int32_t)maxp);
+    // ... unless the split plan launches between one and two rounds of its
+    // 4-wavefront workgroups (768 resident on the 256-CU part at 3 per CU):
+    // its last round would run part-empty, and equal shares do better there
+    // (measured: batch 128 x 8192 tokens 584 vs 666 us, 32 x 32768 592 vs
+    // 619, 128 x 2048 163 vs 174; outside that window the splits win)
+    const int64_t groups = (int64_t)batch * num_kv_heads;
+    const int64_t wgs = groups * ((maxp + pps - 1) / pps);
+    const bool eight_wave = groups <= 256 && wgs == groups;
+    if (!eight_wave && wgs > kSplitRound && wgs <= 2 * kSplitRound && batch <= ekv::kDecodeMaxBalancedBatch)
+      return EKV_DECODE_BALANCED;
+    return pps;
+  }
   // ragged lengths: equal shares of all page-heads per workgroup
   if (batch <= ekv::kDecodeMaxBalancedBatch) return EKV_DECODE_BALANCED;
   int64_t c = (total * num_kv_heads + 4095) / 4096;  // else small splits balance the tail

@@ -167,10 +167,11 @@ size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_
  *   pages_per_split  split-K granularity (0 = automatic; else 1..512), or
  *              EKV_DECODE_BALANCED (batch <= 2,048): all page-heads of the
  *              batch, ordered (sequence, KV head, page), are cut into equal
- *              contiguous ranges, one per workgroup in a single round; a
- *              sequence that one range holds whole is written directly, the
- *              pieces of a cut one are merged by a second kernel.  Evens out
- *              ragged lengths.
+ *              contiguous ranges, one per workgroup, in whole rounds of one
+ *              workgroup per CU (more rounds only to keep each range within
+ *              512 pages); a sequence that one range holds whole is written
+ *              directly, the pieces of a cut one are merged by a second
+ *              kernel.  Evens out ragged lengths.
  *   scratch    device buffer of at least ekv_decode_scratch_bytes(...) bytes
  *              (same arguments), 256-byte aligned; contents are overwritten.
  *              Unused (may be NULL) when that size is 0.

@@ -205,6 +205,35 @@ def _events(n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
 
+def measured_gemm_tflops(reps=20):
+    """A second denominator for the prefill: the best fp16 GEMM rate torch (hipBLASLt) reaches
+    on this part, fp32 accumulation, contiguous operands, median over reps of each of three
+    large shapes (m = n, k); returns (TFLOP/s, "m x n x k")."""
+    import torch
+
+    best = (0.0, "")
+    for n, k in ((8192, 8192), (8192, 16384), (16384, 16384)):
+        a = torch.randn((n, k), device="cuda").half()
+        b = torch.randn((k, n), device="cuda").half()
+        c = torch.empty((n, n), dtype=torch.float16, device="cuda")
+        for _ in range(5):
+            torch.mm(a, b, out=c)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            (e0, e1), = _events(1)
+            e0.record()
+            torch.mm(a, b, out=c)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        del a, b, c
+        tf = 2.0 * n * n * k / (float(np.median(ms)) * 1e-3) / 1e12
+        if tf > best[0]:
+            best = (tf, f"{n} x {n} x {k}")
+    return best
+
+
 def bench_prefill(args):
     """Compact-prefill route, 32 fresh prompts x 8192 tokens: per 4,096-page chunk of 8
     prompts, gather (K copy + E4M3 -> FP16 with scales) then causal FP16 prefill."""
@@ -271,6 +300,7 @@ def bench_prefill(args):
         torch.cuda.synchronize()
         d_ms.append(a.elapsed_time(b))
     d = float(np.mean(d_ms)) * 1e-3
+    gemm, gemm_shape = measured_gemm_tflops()
     rd, wr = bytemodel.gather_bytes(4096, H, D)
     flops = bytemodel.prefill_flops([8192] * 8, Hq, D, causal=True)
     g = float(np.mean(g_ms)) * 1e-3
@@ -284,7 +314,11 @@ def bench_prefill(args):
                                "head dim 128, causal, 4,096-page workspace, 4 chunks of 8 prompts (seed 4)"},
         "prefill": {"avg_chunk_ms": round(p * 1e3, 3), "flops_per_chunk": flops,
                     "tflops": round(flops / p / 1e12, 1), "peak_tflops": MFMA_FP16_PEAK_TFLOPS,
-                    "mfma_frac": round(flops / p / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4)},
+                    "mfma_frac": round(flops / p / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+                    "measured_gemm_tflops": round(gemm, 1),
+                    "frac_of_measured_gemm": round(flops / p / 1e12 / gemm, 4),
+                    "gemm": f"torch.mm fp16 {gemm_shape} (hipBLASLt), best of three large shapes, "
+                            "same process, median of 20 each"},
         "gather": {"avg_chunk_us": round(g * 1e6, 1), "bytes_per_chunk": rd + wr,
                    "gbps": round((rd + wr) / g / 1e9, 1), "peak_gbps": HBM_PEAK_GBPS,
                    "frac": round((rd + wr) / g / 1e9 / HBM_PEAK_GBPS, 4)},

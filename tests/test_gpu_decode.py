@@ -230,3 +230,27 @@ def test_balanced_plan_at_its_batch_limit():
     assert_lse_close(lse, wlse)
     empty = lens == 0
     assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))
+
+
+def test_one_long_sequence_every_plan():
+    """A 131,072-token sequence (8,192 pages) beside a 5-token one, mixed fidelity with
+    value outliers, 32 q / 8 KV heads, head dim 128: the largest split counts (8,192
+    one-page splits) and the longest balanced ranges still match the oracle, and every
+    plan agrees with every other."""
+    step("decode one long sequence, every plan")
+    lens = [131072, 5]
+    c = synth.make_paged_case(131072, lens, 32, 8, 128, compact_frac=0.3,
+                              outlier_frac=0.01, outlier_mult=20.0)
+    dc = DeviceCase(c)
+    want, wlse = oracle_decode(c)
+    host_plan = ekv().ekv_decode_plan_pages_per_split(np.asarray(lens), 8)
+    outs = []
+    for pps in (0, 1, 16, 512, ekv().DECODE_BALANCED, host_plan):
+        out, lse = dc.decode(torch.float32, pages_per_split=pps)
+        assert_close(out, want, what=f"pages_per_split={pps}")
+        assert_lse_close(lse, wlse)
+        outs.append(out)
+    for o in outs[1:]:
+        assert max_abs(o, outs[0]) <= TOL
+    out16, _ = dc.decode(torch.float16)
+    assert f16_bits_equal_rne(out16, outs[0])

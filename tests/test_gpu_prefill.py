@@ -47,7 +47,7 @@ def _oracle_route(pc, prompts, rows, cu, kv_start, apply_scale=True, causal=True
     return oracle.prefill_attention(c.q[rows], wk, wv, cu, kv_start, causal, c.sm_scale, rows=sample)
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (8, 2, 128), (16, 2, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (8, 2, 128), (16, 2, 64), (16, 8, 128), (4, 2, 64)])
 def test_prefill_route_ragged_prompts(hq, hkv, d):
     step(f"prefill ragged hq={hq} hkv={hkv} d={d}")
     lens = [1, 17, 100, 257, 64, 130]

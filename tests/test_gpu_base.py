@@ -56,7 +56,8 @@ def test_pack_pairs_bit_exact_in_place_and_skips():
         assert np.array_equal(vt.cpu().numpy().view(np.uint16), wv.view(np.uint16)), (hkv, d)
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (16, 2, 128), (8, 1, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (16, 2, 128), (8, 1, 64), (16, 8, 128),
+                                      (4, 2, 64)])
 def test_general_path_target_compact_base_mix(hq, hkv, d):
     step(f"elastic decode, flag table, hq={hq} hkv={hkv} d={d}")
     e = synth.make_elastic_case(61 + d, [300, 1029, 64, 777, 16], hq, hkv, d, sink_pages=2, recent_pages=4,

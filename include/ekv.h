@@ -102,6 +102,11 @@ typedef struct {
 /* Version of this ABI (EKV_ABI_VERSION). */
 int32_t ekv_abi_version(void);
 
+/* Identity of the sources this library was built from: the sha256 (hex) of
+ * the .hip and .hpp files of the kernel sources and of this header, taken by
+ * the build script. */
+const char* ekv_build_id(void);
+
 /* Static description of a status code. */
 const char* ekv_status_string(ekv_status s);
 
@@ -171,10 +176,13 @@ size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_
  *              workgroup per CU (more rounds only to keep each range within
  *              512 pages); a sequence that one range holds whole is written
  *              directly, the pieces of a cut one are merged by a second
- *              kernel.  Evens out ragged lengths.
+ *              kernel.  Evens out ragged lengths.  Split plans with more
+ *              than one split per sequence also end with the merge kernel.
  *   scratch    device buffer of at least ekv_decode_scratch_bytes(...) bytes
- *              (same arguments), 256-byte aligned; contents are overwritten.
- *              Unused (may be NULL) when that size is 0.
+ *              (same arguments), 256-byte aligned; contents are overwritten
+ *              and need no initial value.  Unused (may be NULL) when that
+ *              size is 0.  Calls that overlap in time must not share a
+ *              scratch buffer.
  * Sequences that reference an out-of-range page id or an unknown flag get
  * NaN outputs and NaN lse.
  */
@@ -362,13 +370,16 @@ ekv_status ekv_pack_base_pairs(const ekv_paged_kv* kv, const int32_t* src_a, con
                                const int32_t* dst, int32_t n_pairs, void* stream);
 
 /*
- * Diagnostic for the device E4M3 decoding used by the kernels: converts n
- * codes to fp16.  method 0 = the decode kernel's path (codes packed four per
- * 32-bit word, scale 1), 2 = the same path with scale 2^-7 (so out =
- * fp16(e4m3 * 2^-7)), 1 = the gather kernel's path.  codes u8 [n], out fp16
- * [n] (device).  Other methods return EKV_ERR_INVALID_ARG.
+ * Diagnostic for the device E4M3 decoding used by the kernels: out[i] =
+ * fp16(e4m3(codes[i]) * 2^scale_exp), scale_exp in -126..127.  method 0 =
+ * the decode kernel's conversion instruction (codes packed four per 32-bit
+ * word, the instruction's power-of-two scale; the decode kernel hands it
+ * only exponents in -15..7, where every result is exact); method 1 = the
+ * gather's arithmetic (fp32 product rounded to nearest even, then fp16
+ * rounded to nearest even).  codes u8 [n], out fp16 [n] (device).  Other
+ * methods or exponents return EKV_ERR_INVALID_ARG.
  */
-ekv_status ekv_e4m3_to_f16(const uint8_t* codes, int32_t n, void* out, int32_t method,
+ekv_status ekv_e4m3_to_f16(const uint8_t* codes, int32_t n, void* out, int32_t method, int32_t scale_exp,
                            void* stream);
 
 #ifdef __cplusplus

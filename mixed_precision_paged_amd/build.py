@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -28,6 +29,33 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+
+
+def source_files():
+    """The files libekv.so is built from: csrc/*.hip, csrc/*.hpp and include/ekv.h."""
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")))
+    return files + [os.path.join(ROOT, "include", "ekv.h")]
+
+
+def source_hash() -> str:
+    """sha256 over the sources' names and bytes; baked into the library as ekv_build_id()."""
+    h = hashlib.sha256()
+    for f in source_files():
+        h.update(os.path.relpath(f, ROOT).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
+def check_library_matches_sources() -> None:
+    """Raise if the loaded libekv.so was not built from the sources in this tree."""
+    from . import ekv
+
+    built, here = ekv.ekv_build_id(), source_hash()
+    if built != here:
+        raise RuntimeError(f"libekv.so was built from other sources (build id {built[:16]}, tree {here[:16]}): "
+                           "rebuild with `python -m mixed_precision_paged_amd.build`")
 
 
 def _hipcc() -> str:
@@ -55,10 +83,11 @@ def build(verbose: bool = False) -> str:
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = []
     jobs = []
+    build_id = f"-DEKV_BUILD_ID=\"{source_hash()}\""
     for src in sources:
         obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
-        jobs.append([hipcc, *COMMON, "-c", src, "-o", obj])
+        jobs.append([hipcc, *COMMON, build_id, "-c", src, "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"

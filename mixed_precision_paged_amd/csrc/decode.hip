@@ -14,8 +14,9 @@
 //   workgroup = (split of pages, KV head g, sequence b); its wavefronts take
 //   the split's pages round-robin, one page (16 tokens x D) at a time, with
 //   the next page's loads in flight while the current one computes.  Page
-//   ids and flags of the split are staged in LDS once.  Loads go through a
-//   buffer descriptor that spans exactly one page of one KV head.
+//   ids, flags and value scales of the split are staged in LDS once.
+//   Loads go through a buffer descriptor that spans exactly one page of one
+//   KV head.
 //   QK^T: v_mfma_f32_16x16x32_f16 computes S^T = K Q^T with the page's 16
 //   tokens as rows and the G = Hq/Hkv query heads as columns (padded to 16),
 //   so the G heads share every K/V load.
@@ -26,8 +27,10 @@
 //   P goes in as an fp16 hi + lo pair (two MFMAs), p = hi + lo to ~22 bits.
 //   Compact pages expand their E4M3 bytes in registers with the gfx950
 //   scaled conversion by the power-of-two part 2^e of the page-head scale
-//   (exact: code * 2^e is an fp16 value); the mantissa part f of the scale
-//   multiplies p in fp32.  Both kinds meet in one fp16-value PV path.  The
+//   (exact: code * 2^e is an fp16 value for e in [-15, 7]; a scale outside
+//   that range expands by the nearest end of it and rescales the page's
+//   P.V products in fp32 by the remaining power of two); the mantissa part
+//   f of the scale multiplies p in fp32.  Both kinds meet in one fp16-value PV path.  The
 //   flag is per page, so the branch is wavefront-uniform.
 //   End of split: wavefronts merge through LDS.  One split per sequence: the
 //   workgroup writes the normalized output and LSE.  Several: it writes
@@ -57,6 +60,9 @@ constexpr int kBalancedMaxPages = 512;  // balanced plan: pages per range (LDS s
 constexpr int kBalancedWaves = 8;       // balanced plan: wavefronts per workgroup
 constexpr int kSlots = 2;             // register page buffers per wavefront (pages in flight + 1)
 constexpr int kMinWaves = 2;          // occupancy bound (wavefronts per SIMD) for G*D < 1024
+constexpr int kExpLo = -15;           // code * 2^x is exact in fp16 for every E4M3 code iff
+constexpr int kExpHi = 7;             //   x in [kExpLo, kExpHi] (2^-9 * 2^-15 = 2^-24; 448 * 2^7 < 65504)
+constexpr int kMaxShift = 60;         // bound of the fp32 rescale of acc for out-of-range scales
 
 template <int D>
 struct PageRegs {
@@ -171,7 +177,8 @@ template <int D, int G>
 struct State {
   f16x8 qb[D / 32];      // Q[head l%16][32kb + 8(l/16) .. +8]: MFMA B operand (0 for head >= G)
   float m, l;            // running max (log2 units) and partial sum of head l%16 (this lane's tokens)
-  f32x4 acc[D / 16];     // O[head 4(l/16)+i][d = (D/16)(l%16) + e] in acc[e][i]
+  f32x4 acc[D / 16];     // O[head 4(l/16)+i][d = (D/16)(l%16) + e] * 2^-aexp in acc[e][i]
+  int aexp;              // wavefront-uniform power-of-two offset of acc (0 unless scales are extreme)
 };
 
 __device__ __forceinline__ f16x4 pack4(float a, float b, float c, float d) {
@@ -191,10 +198,19 @@ __device__ __forceinline__ void process_page(State<D, G>& st, PageRegs<D>& r, co
                                              int kind, float scale, int pg, int len, int lane) {
   constexpr int NE = D / 16;  // PV MFMAs (d columns per lane)
   const int tq = lane >> 4;
-  // Compact scale s = 2^e * f, f in [1, 2): the conversion applies the exact power of two,
-  // p carries f.  (Scales are positive normal fp32 values.)
+  // Compact scale s = 2^sexp * f, f in [1, 2): the conversion applies a power of two, p
+  // carries f.  code * 2^x is an fp16 value for every E4M3 code only for x in [kExpLo,
+  // kExpHi], so the conversion gets x = sexp - shift in that range and the page's P.V
+  // products need the factor 2^shift.  acc is kept as true value * 2^-st.aexp; a page
+  // whose shift differs from st.aexp first rescales acc by 2^(st.aexp - shift) (a power
+  // of two: exact while acc stays normal) and sets st.aexp = shift.  Scales derived from fp16 values (the cache writer) have sexp in
+  // [-33, 7]; |shift| is bounded by kMaxShift.  (Scales are positive normal fp32 values.)
   const uint32_t sbits = kind == 1 ? __builtin_bit_cast(uint32_t, scale) : 0x3F800000u;
-  const float s_pow2 = as_f32(sbits & 0x7F800000u);
+  const int sexp = (int)((sbits >> 23) & 0xFFu) - 127;
+  const int shift = sexp < kExpLo   ? max(sexp - kExpLo, -kMaxShift)
+                    : sexp > kExpHi ? min(sexp - kExpHi, kMaxShift)
+                                    : 0;
+  const float s_pow2 = as_f32((uint32_t)(sexp - shift + 127) << 23);
   const float s_frac = as_f32((sbits & 0x807FFFFFu) | 0x3F800000u);
   const bool partial = pg * kPage + kPage > len;  // wavefront-uniform
 
@@ -239,6 +255,14 @@ __device__ __forceinline__ void process_page(State<D, G>& st, PageRegs<D>& r, co
       for (int e = 0; e < NE; ++e) st.acc[e][i] *= ai;
     }
     st.m = mnew;
+  }
+  if (shift != st.aexp) {  // wavefront-uniform; only for page-head scales outside the exact range
+    const float k = as_f32((uint32_t)(st.aexp - shift + 127) << 23);  // 2^(aexp - shift), exact
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.acc[e][i] *= k;
+    st.aexp = shift;
   }
   float pv[4];
 #pragma unroll
@@ -313,6 +337,7 @@ struct PieceSmem {
   float l[NW][G];
   int bad[NW];
   int meta[MAXP];
+  float scale[MAXP];  // page-head value scale of each compact page of the piece (1 otherwise)
 };
 
 // MODE 0: every page has kind p.uniform_kind (no flag table); 1: per-page flags
@@ -345,12 +370,14 @@ __device__ __forceinline__ void run_piece(const DecodeParams& p, SM& sm, int b, 
   }
   st.m = kNegBig;
   st.l = 0.f;
+  st.aexp = 0;
 #pragma unroll
   for (int e = 0; e < NE; ++e) st.acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Stage this split's page metadata in LDS once: (phys << KBITS | kind), or
-  // -1 for an out-of-range id or unknown flag.  Per-page reads are then LDS
-  // reads, which never wait on the vector-memory counter of in-flight pages.
+  // -1 for an out-of-range id or unknown flag, and each compact page's scale.
+  // Per-page reads are then LDS reads, which never wait on the vector-memory
+  // counter of in-flight pages.
   // A BASE page id names half (id & 1) of TARGET block id >> 1.
   {
     const int32_t* pt = p.page_table + (int64_t)b * p.pt_stride;
@@ -365,6 +392,7 @@ __device__ __forceinline__ void run_piece(const DecodeParams& p, SM& sm, int b, 
                       (kind == 1 && (unsigned)phys < (unsigned)p.n_compact) ||
                       (HAS_BASE && kind == 2 && (unsigned)phys < 2u * (unsigned)p.n_target);
       sm.meta[i] = ok ? (phys << KBITS) | kind : -1;
+      sm.scale[i] = ok && kind == 1 ? p.v_scale[(int64_t)phys * p.num_kv_heads + g] : 1.0f;
     }
   }
   __syncthreads();
@@ -412,7 +440,7 @@ __device__ __forceinline__ void run_piece(const DecodeParams& p, SM& sm, int b, 
       kbytes = 0u;
       vbytes = 0u;
     }
-    sl.scale = sl.kind == 1 ? p.v_scale[(int64_t)phys * p.num_kv_heads + g] : 1.0f;
+    sl.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sm.scale[pq - pbeg])));
     load_page<D, HAS_BASE>(sl.r, sl.kind, kb, vb, kbytes, vbytes, kqoff, kqoff8, voff16, voff8, krow, vrow);
   };
   // kSlots register page buffers: pages pg+4 .. pg+4(kSlots-1) load while page pg
@@ -451,6 +479,13 @@ __device__ __forceinline__ void run_piece(const DecodeParams& p, SM& sm, int b, 
   // its output rows are acc[e][i] for h = 4(l/16)+i, d = (D/16)(l%16) + e.
   float L = st.l + shfl_xor(st.l, 16);
   L += shfl_xor(L, 32);
+  if (st.aexp != 0) {  // back to true values (exact power-of-two scaling)
+    const float k = as_f32((uint32_t)(st.aexp + 127) << 23);
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.acc[e][i] *= k;
+  }
   {
     const int tq = lane >> 4, dq = lane & 15;
 #pragma unroll

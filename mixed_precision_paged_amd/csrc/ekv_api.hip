@@ -10,8 +10,10 @@
 #include "ekv_internal.hpp"
 
 namespace {
-
 thread_local char g_last_error[512] = "";
+}  // namespace
+
+namespace ekv {
 
 ekv_status fail(ekv_status s, const char* fmt, ...) {
   va_list ap;
@@ -30,6 +32,14 @@ ekv_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(EKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+}  // namespace ekv
+
+namespace {
+
+using ekv::fail;
+using ekv::hip_status;
+using ekv::ok;
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -75,6 +85,11 @@ constexpr int64_t kSplitRound = 768;
 extern "C" {
 
 int32_t ekv_abi_version(void) { return EKV_ABI_VERSION; }
+
+#ifndef EKV_BUILD_ID
+#define EKV_BUILD_ID "unknown"
+#endif
+const char* ekv_build_id(void) { return EKV_BUILD_ID; }
 
 const char* ekv_status_string(ekv_status s) {
   switch (s) {
@@ -143,13 +158,13 @@ size_t ekv_decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_
 
 }  // extern "C"
 
-namespace {
+namespace ekv {
 
-ekv_status decode_impl(const ekv_paged_kv* kv, const void* q, int32_t batch, int32_t num_q_heads,
-                       const int32_t* page_table, int32_t pt_stride, const uint8_t* fidelity,
-                       const int32_t* base_bounds, int32_t has_base, const int32_t* seq_lens,
-                       int32_t max_seq_len, float sm_scale, void* out, ekv_dtype out_dtype, float* lse,
-                       int32_t pages_per_split, void* scratch, size_t scratch_bytes, void* stream) {
+ekv_status decode_entry(const ekv_paged_kv* kv, const void* q, int32_t batch, int32_t num_q_heads,
+                        const int32_t* page_table, int32_t pt_stride, const uint8_t* fidelity,
+                        const int32_t* base_bounds, int32_t has_base, const int32_t* seq_lens,
+                        int32_t max_seq_len, float sm_scale, void* out, ekv_dtype out_dtype, float* lse,
+                        int32_t pages_per_split, void* scratch, size_t scratch_bytes, void* stream) {
   if (!kv) return fail(EKV_ERR_INVALID_ARG, "kv descriptor is NULL");
   ekv_status s = check_geometry(num_q_heads, kv->num_kv_heads, kv->head_dim);
   if (s != EKV_OK) return s;
@@ -233,7 +248,7 @@ ekv_status decode_impl(const ekv_paged_kv* kv, const void* q, int32_t batch, int
   return hip_status(ekv::launch_decode(p, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
-}  // namespace
+}  // namespace ekv
 
 extern "C" {
 
@@ -243,7 +258,7 @@ ekv_status ekv_decode_attention(const ekv_paged_kv* kv, const void* q, int32_t b
                                 int32_t max_seq_len, float sm_scale, void* out, ekv_dtype out_dtype,
                                 float* lse, int32_t pages_per_split, void* scratch,
                                 size_t scratch_bytes, void* stream) {
-  return decode_impl(kv, q, batch, num_q_heads, page_table, pt_stride, fidelity, nullptr, 0, seq_lens,
+  return ekv::decode_entry(kv, q, batch, num_q_heads, page_table, pt_stride, fidelity, nullptr, 0, seq_lens,
                      max_seq_len, sm_scale, out, out_dtype, lse, pages_per_split, scratch, scratch_bytes,
                      stream);
 }
@@ -256,7 +271,7 @@ ekv_status ekv_decode_attention_elastic(const ekv_paged_kv* kv, const void* q, i
                                         void* out, ekv_dtype out_dtype, float* lse,
                                         int32_t pages_per_split, void* scratch, size_t scratch_bytes,
                                         void* stream) {
-  return decode_impl(kv, q, batch, num_q_heads, page_table, pt_stride, fidelity, base_bounds, has_base,
+  return ekv::decode_entry(kv, q, batch, num_q_heads, page_table, pt_stride, fidelity, base_bounds, has_base,
                      seq_lens, max_seq_len, sm_scale, out, out_dtype, lse, pages_per_split, scratch,
                      scratch_bytes, stream);
 }
@@ -477,12 +492,14 @@ ekv_status ekv_pack_base_pairs(const ekv_paged_kv* kv, const int32_t* src_a, con
   return hip_status(ekv::launch_pack_base(p, static_cast<hipStream_t>(stream)), "pack launch");
 }
 
-ekv_status ekv_e4m3_to_f16(const uint8_t* codes, int32_t n, void* out, int32_t method, void* stream) {
+ekv_status ekv_e4m3_to_f16(const uint8_t* codes, int32_t n, void* out, int32_t method, int32_t scale_exp,
+                           void* stream) {
   if (n < 0) return fail(EKV_ERR_INVALID_ARG, "n %d < 0", n);
-  if (method < 0 || method > 2) return fail(EKV_ERR_INVALID_ARG, "method must be 0, 1 or 2");
+  if (method < 0 || method > 1) return fail(EKV_ERR_INVALID_ARG, "method must be 0 or 1");
+  if (scale_exp < -126 || scale_exp > 127) return fail(EKV_ERR_INVALID_ARG, "scale_exp %d outside -126..127", scale_exp);
   if (n == 0) return ok();
   if (!codes || !out) return fail(EKV_ERR_INVALID_ARG, "codes and out are required");
-  return hip_status(ekv::launch_e4m3_to_f16(codes, n, static_cast<uint16_t*>(out), method,
+  return hip_status(ekv::launch_e4m3_to_f16(codes, n, static_cast<uint16_t*>(out), method, scale_exp,
                                             static_cast<hipStream_t>(stream)),
                     "e4m3 launch");
 }

@@ -5,7 +5,23 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ekv.h"
+
 namespace ekv {
+
+// Status helpers of the C ABI: `fail` records a thread-local message for
+// ekv_last_error(), `ok` clears it, `hip_status` maps a HIP error.
+ekv_status fail(ekv_status s, const char* fmt, ...);
+ekv_status ok();
+ekv_status hip_status(hipError_t e, const char* what);
+
+// Argument checks, plan and launch of ekv_decode_attention(_elastic) with the
+// scratch buffer given (shared by the allocation-free entry point).
+ekv_status decode_entry(const ekv_paged_kv* kv, const void* q, int32_t batch, int32_t num_q_heads,
+                        const int32_t* page_table, int32_t pt_stride, const uint8_t* fidelity,
+                        const int32_t* base_bounds, int32_t has_base, const int32_t* seq_lens,
+                        int32_t max_seq_len, float sm_scale, void* out, ekv_dtype out_dtype, float* lse,
+                        int32_t pages_per_split, void* scratch, size_t scratch_bytes, void* stream);
 
 struct DecodeParams {
   const uint16_t* k_target;
@@ -116,6 +132,7 @@ struct PackParams {
 
 // Split plan shared by the scratch query and the launch.
 int32_t decode_auto_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages);
+
 size_t decode_scratch_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t n_splits);
 // Balanced plan: workgroups for a batch whose longest sequence has max_pages
@@ -132,6 +149,6 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
 hipError_t launch_pack_base(const PackParams& p, hipStream_t stream);
 hipError_t launch_e4m3_to_f16(const uint8_t* codes, int32_t n, uint16_t* out, int32_t method,
-                              hipStream_t stream);
+                              int32_t scale_exp, hipStream_t stream);
 
 }  // namespace ekv

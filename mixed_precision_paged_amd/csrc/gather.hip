@@ -68,20 +68,24 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherParams p) 
   dv[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// Diagnostic: method 0/2 = the decode kernel's packed path (4 codes per word,
-// both word halves, power-of-two scale 1 or 2^-7); method 1 = the gather path.
-__global__ void e4m3_to_f16_kernel(const uint8_t* codes, int32_t n, uint16_t* out, int32_t method) {
+// Diagnostic: code * 2^scale_exp to fp16.  method 0 = the conversion the
+// decode kernel uses (4 codes per word, both word halves, the instruction's
+// power-of-two scale); method 1 = the gather's arithmetic (exact fp32 value
+// times the fp32 scale, rounded to nearest even, then to fp16 nearest even).
+__global__ void e4m3_to_f16_kernel(const uint8_t* codes, int32_t n, uint16_t* out, int32_t method,
+                                   int32_t scale_exp) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (4 * i >= n) return;
   uint32_t w = 0;
   for (int k = 0; k < 4 && 4 * i + k < n; ++k) w |= (uint32_t)codes[4 * i + k] << (8 * k);
+  const float s = __builtin_amdgcn_ldexpf(1.0f, scale_exp);
   uint32_t r[2];
   if (method == 1) {
+#pragma clang fp contract(off)
     const f32x2 a = e4m3x2_f32(w, false), b = e4m3x2_f32(w, true);
-    r[0] = pack_rne(a.x, a.y);
-    r[1] = pack_rne(b.x, b.y);
+    r[0] = pack_rne(a.x * s, a.y * s);
+    r[1] = pack_rne(b.x * s, b.y * s);
   } else {
-    const float s = method == 2 ? 0.0078125f : 1.0f;
     r[0] = bits(e4m3x2_scaled_f16(w, s, false));
     r[1] = bits(e4m3x2_scaled_f16(w, s, true));
   }
@@ -99,10 +103,10 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_e4m3_to_f16(const uint8_t* codes, int32_t n, uint16_t* out, int32_t method,
-                              hipStream_t stream) {
+                              int32_t scale_exp, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(e4m3_to_f16_kernel, dim3((n + 1023) / 1024), dim3(256), 0, stream, codes, n,
-                     out, method);
+                     out, method, scale_exp);
   return hipGetLastError();
 }
 

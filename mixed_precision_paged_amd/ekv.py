@@ -40,7 +40,7 @@ EXPORTED = (
     "ekv_decode_plan_pages_per_split", "ekv_decode_scratch_bytes", "ekv_decode_attention",
     "ekv_decode_attention_elastic", "ekv_gather_compact_pages", "ekv_prefill_attention",
     "ekv_prefill_paged_attention", "ekv_append_tokens", "ekv_quantize_pages", "ekv_pack_base_pairs",
-    "ekv_e4m3_to_f16",
+    "ekv_e4m3_to_f16", "ekv_build_id",
 )
 
 
@@ -55,6 +55,7 @@ class PagedKV(ctypes.Structure):
 
 _i32, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 _lib.ekv_abi_version.restype = _i32
+_lib.ekv_build_id.restype = ctypes.c_char_p
 _lib.ekv_status_string.restype = ctypes.c_char_p
 _lib.ekv_status_string.argtypes = [ctypes.c_int]
 _lib.ekv_last_error.restype = ctypes.c_char_p
@@ -90,7 +91,7 @@ _lib.ekv_quantize_pages.restype = ctypes.c_int
 _lib.ekv_quantize_pages.argtypes = [ctypes.POINTER(PagedKV), _vp, _vp, ctypes.c_int64, _vp, _vp, _vp,
                                     _i32, _vp]
 _lib.ekv_e4m3_to_f16.restype = ctypes.c_int
-_lib.ekv_e4m3_to_f16.argtypes = [_vp, _i32, _vp, _i32, _vp]
+_lib.ekv_e4m3_to_f16.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp]
 
 
 class EkvError(RuntimeError):
@@ -101,6 +102,10 @@ class EkvError(RuntimeError):
 
 def ekv_abi_version() -> int:
     return int(_lib.ekv_abi_version())
+
+
+def ekv_build_id() -> str:
+    return _lib.ekv_build_id().decode()
 
 
 def ekv_status_string(status: int) -> str:
@@ -144,6 +149,30 @@ def _arg(t: Optional[torch.Tensor], name: str, dtypes=None) -> Optional[int]:
 def _same_shape(a: Optional[torch.Tensor], b: Optional[torch.Tensor], what: str) -> None:
     if a is not None and b is not None and tuple(a.shape) != tuple(b.shape):
         raise ValueError(f"{what}: shapes {tuple(a.shape)} and {tuple(b.shape)} differ")
+
+
+def _expect(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_decode_shapes(kv: PagedKV, q, page_table, seq_lens, out, lse, rows_of=None) -> None:
+    """Shapes the decode entry points assume, checked before any launch."""
+    _expect(q.dim() == 3, f"q must be [batch, num_q_heads, head_dim], got {tuple(q.shape)}")
+    batch, hq, d = q.shape
+    _expect(d == kv.head_dim, f"q has head dim {d}, the pools {kv.head_dim}")
+    _expect(page_table.dim() == 2 and int(page_table.shape[0]) == batch,
+            f"page_table must have one row per sequence ({batch}), got {tuple(page_table.shape)}")
+    _expect(tuple(seq_lens.shape) == (batch,), f"seq_lens must be [{batch}], got {tuple(seq_lens.shape)}")
+    _expect(tuple(out.shape) == tuple(q.shape), f"out must be {tuple(q.shape)}, got {tuple(out.shape)}")
+    _expect(lse is None or tuple(lse.shape) == (batch, hq), f"lse must be [{batch}, {hq}], got "
+            f"{None if lse is None else tuple(lse.shape)}")
+
+
+def _check_prefill_out(q, out, lse) -> None:
+    _expect(tuple(out.shape) == tuple(q.shape), f"out must be {tuple(q.shape)}, got {tuple(out.shape)}")
+    _expect(lse is None or tuple(lse.shape) == tuple(q.shape[:2]),
+            f"lse must be {tuple(q.shape[:2])}, got {None if lse is None else tuple(lse.shape)}")
 
 
 def _kv_ref(kv: PagedKV):
@@ -209,6 +238,7 @@ def ekv_decode_attention(kv: PagedKV, q: torch.Tensor, page_table: torch.Tensor,
                          scratch: Optional[torch.Tensor] = None, pages_per_split: int = 0,
                          stream=None) -> None:
     """GQA decode over paged TARGET/compact KV (see ekv.h).  Writes ``out`` (and ``lse``)."""
+    _check_decode_shapes(kv, q, page_table, seq_lens, out, lse)
     batch, hq, _ = q.shape
     _same_shape(page_table, fidelity, "page_table and fidelity")
     if scratch is None:
@@ -231,7 +261,10 @@ def ekv_decode_attention_elastic(kv: PagedKV, q: torch.Tensor, page_table: torch
                                  stream=None) -> None:
     """Decode over TARGET / compact / ElasticKV BASE pages (see ekv.h): per-page flags
     (0, 1, 2) or per-sequence BASE bounds [B, 2] for TARGET-BASE-TARGET layouts."""
+    _check_decode_shapes(kv, q, page_table, seq_lens, out, lse)
     batch, hq, _ = q.shape
+    _expect(base_bounds is None or tuple(base_bounds.shape) == (batch, 2),
+            f"base_bounds must be [{batch}, 2], got {None if base_bounds is None else tuple(base_bounds.shape)}")
     _same_shape(page_table, fidelity, "page_table and fidelity")
     if scratch is None:
         need = ekv_decode_scratch_bytes(batch, hq, kv.num_kv_heads, kv.head_dim, max_seq_len,
@@ -257,7 +290,14 @@ def ekv_pack_base_pairs(kv: PagedKV, src_a: torch.Tensor, src_b: torch.Tensor, d
 def ekv_gather_compact_pages(kv: PagedKV, page_ids: torch.Tensor, apply_scale: bool,
                              ws_k: torch.Tensor, ws_v: torch.Tensor, n_pages: Optional[int] = None,
                              stream=None) -> None:
-    """Gather compact pages into the FP16 workspace (see ekv.h)."""
+    """Gather compact pages into the FP16 workspace (see ekv.h).
+
+    ws_k, ws_v: [capacity, 16, Hkv, D] fp16 (the capacity is their first dimension)."""
+    page = (PAGE_SIZE, kv.num_kv_heads, kv.head_dim)
+    for name, ws in (("ws_k", ws_k), ("ws_v", ws_v)):
+        _expect(ws.dim() == 4 and tuple(ws.shape[1:]) == page,
+                f"{name} must be [capacity, {', '.join(map(str, page))}], got {tuple(ws.shape)}")
+    _expect(page_ids.dim() == 1, f"page_ids must be one-dimensional, got {tuple(page_ids.shape)}")
     n = int(page_ids.shape[0]) if n_pages is None else int(n_pages)
     if n > int(page_ids.shape[0]):
         raise ValueError(f"n_pages {n} exceeds the {int(page_ids.shape[0])} page ids given")
@@ -274,7 +314,14 @@ def ekv_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """Causal FP16 prefill over contiguous K/V rows (see ekv.h).
 
     q: [T, Hq, D]; k, v: [R, Hkv, D] (or the workspace view [pages, 16, Hkv, D])."""
+    _expect(q.dim() == 3, f"q must be [rows, num_q_heads, head_dim], got {tuple(q.shape)}")
     q_rows, hq, d = q.shape
+    _expect(k.dim() in (3, 4), f"k must be [rows, Hkv, D] or [pages, 16, Hkv, D], got {tuple(k.shape)}")
+    _expect(k.dim() == 3 or int(k.shape[1]) == PAGE_SIZE, f"workspace pages hold {PAGE_SIZE} rows, got {tuple(k.shape)}")
+    _expect(kv_start.dim() == 1 and tuple(cu_seqlens_q.shape) == (int(kv_start.shape[0]) + 1,),
+            f"cu_seqlens_q must have n_prompts + 1 = {int(kv_start.shape[0]) + 1} entries, got "
+            f"{tuple(cu_seqlens_q.shape)}")
+    _check_prefill_out(q, out, lse)
     hkv = int(k.shape[-2])
     if int(k.shape[-1]) != d:
         raise ValueError(f"K rows have head dim {int(k.shape[-1])}, queries {d}")
@@ -294,6 +341,12 @@ def ekv_prefill_paged_attention(kv: PagedKV, q: torch.Tensor, cu_seqlens_q: torc
     """Causal FP16 prefill straight from each prompt's pages (see ekv.h).
 
     q: [T, Hq, D]; page_table: [n_prompts, stride] int32; fidelity: same shape uint8 or None."""
+    _expect(q.dim() == 3, f"q must be [rows, num_q_heads, head_dim], got {tuple(q.shape)}")
+    _expect(int(q.shape[2]) == kv.head_dim, f"q has head dim {int(q.shape[2])}, the pools {kv.head_dim}")
+    _expect(page_table.dim() == 2 and tuple(cu_seqlens_q.shape) == (int(page_table.shape[0]) + 1,),
+            f"cu_seqlens_q must have one entry per page-table row plus one, got {tuple(cu_seqlens_q.shape)} "
+            f"for page_table {tuple(page_table.shape)}")
+    _check_prefill_out(q, out, lse)
     q_rows, hq, _ = q.shape
     _same_shape(page_table, fidelity, "page_table and fidelity")
     _check(_lib.ekv_prefill_paged_attention(
@@ -308,6 +361,8 @@ def ekv_append_tokens(kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor,
     """Write new tokens' K/V rows ([n, Hkv, D] fp16) into TARGET slots (see ekv.h).
     ``kv`` must describe writable TARGET pools."""
     _same_shape(k_new, v_new, "k_new and v_new")
+    _expect(tuple(k_new.shape[-2:]) == (kv.num_kv_heads, kv.head_dim),
+            f"k_new rows must be [{kv.num_kv_heads}, {kv.head_dim}], got {tuple(k_new.shape)}")
     if k_new.numel() != int(slot_mapping.shape[0]) * kv.num_kv_heads * kv.head_dim:
         raise ValueError("k_new/v_new must hold one [Hkv, D] row per slot_mapping entry")
     _check(_lib.ekv_append_tokens(_kv_ref(kv), _arg(k_new, "k_new", _F16), _arg(v_new, "v_new", _F16),
@@ -325,6 +380,8 @@ def ekv_quantize_pages(kv: PagedKV, k_src: torch.Tensor, v_src: torch.Tensor,
     _same_shape(k_src, v_src, "k_src and v_src")
     _same_shape(src_row_start, dst_pages, "src_row_start and dst_pages")
     _same_shape(n_valid, dst_pages, "n_valid and dst_pages")
+    _expect(tuple(k_src.shape[-2:]) == (kv.num_kv_heads, kv.head_dim),
+            f"k_src rows must be [{kv.num_kv_heads}, {kv.head_dim}], got {tuple(k_src.shape)}")
     rows = k_src.numel() // (kv.num_kv_heads * kv.head_dim)
     _check(_lib.ekv_quantize_pages(_kv_ref(kv), _arg(k_src, "k_src", _F16), _arg(v_src, "v_src", _F16),
                                    rows, _arg(src_row_start, "src_row_start", _I32),
@@ -332,9 +389,10 @@ def ekv_quantize_pages(kv: PagedKV, k_src: torch.Tensor, v_src: torch.Tensor,
                                    int(dst_pages.shape[0]), _stream(stream)))
 
 
-def ekv_e4m3_to_f16(codes: torch.Tensor, out: torch.Tensor, method: int, stream=None) -> None:
-    """Diagnostic: device E4M3 -> fp16 conversion (0 = decode path, 1 = gather path)."""
+def ekv_e4m3_to_f16(codes: torch.Tensor, out: torch.Tensor, method: int, scale_exp: int = 0,
+                    stream=None) -> None:
+    """Diagnostic: device E4M3 -> fp16 of code * 2^scale_exp (0 = decode path, 1 = gather path)."""
     if out.numel() != codes.numel():
         raise ValueError("out must hold one fp16 value per code")
     _check(_lib.ekv_e4m3_to_f16(_arg(codes, "codes", _U8), int(codes.numel()), _arg(out, "out", _F16),
-                                int(method), _stream(stream)))
+                                int(method), int(scale_exp), _stream(stream)))

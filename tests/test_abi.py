@@ -22,10 +22,17 @@ def _declared():
 
 def test_every_declared_function_is_exported():
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(ekv._lib, n), n
     assert sorted(ekv.EXPORTED) == names
+
+
+def test_library_was_built_from_these_sources():
+    from mixed_precision_paged_amd import build
+
+    assert len(ekv.ekv_build_id()) == 64
+    build.check_library_matches_sources()
 
 
 def test_version_and_status_strings():
@@ -84,11 +91,14 @@ def test_split_plan_and_scratch_size():
     # 256 (sequence, KV head) groups: one split each, no partials
     assert ekv.ekv_decode_pages_per_split(32, 8, 8192) == 512
     assert ekv.ekv_decode_scratch_bytes(32, 32, 8, 128, 8192, 0) == 0
+    up = lambda n: (n + 255) // 256 * 256
+
+    def split_scratch(batch, hq, hkv, d, splits):  # acc | (max, sum) per (b, q head, split)
+        rows = batch * hq * splits
+        return up(rows * d * 4) + rows * 2 * 4
+
     for pps, splits in ((256, 2), (128, 4), (100, 6)):
-        rows = 32 * 32 * splits
-        acc = rows * 128 * 4
-        expect = ((acc + 255) // 256) * 256 + rows * 2 * 4
-        assert ekv.ekv_decode_scratch_bytes(32, 32, 8, 128, 8192, pps) == expect
+        assert ekv.ekv_decode_scratch_bytes(32, 32, 8, 128, 8192, pps) == split_scratch(32, 32, 8, 128, splits)
     # 128 groups: about 512 split workgroups of pages
     assert ekv.ekv_decode_pages_per_split(16, 8, 8192) == 128
     # 512 groups: one split each
@@ -101,7 +111,7 @@ def test_split_plan_and_scratch_size():
     recs = 2048 * 2 * 4
     assert ekv.ekv_decode_scratch_bytes(64, 32, 8, 128, 32768, ekv.DECODE_BALANCED) == \
         ((recs * 128 * 4 + 255) // 256) * 256 + recs * 2 * 4
-    assert ekv.ekv_decode_scratch_bytes(2, 4, 1, 64, 64, 1) == ((2 * 4 * 4 * 64 * 4 + 255) // 256) * 256 + 2 * 4 * 4 * 8
+    assert ekv.ekv_decode_scratch_bytes(2, 4, 1, 64, 64, 1) == split_scratch(2, 4, 1, 64, 4)
     assert ekv.ekv_decode_scratch_bytes(0, 4, 1, 64, 64, 1) == 0
 
 
@@ -154,9 +164,11 @@ def test_prefill_validation():
 
 def test_e4m3_diagnostic_validation():
     f = ekv._lib.ekv_e4m3_to_f16
-    assert f(FAKE, 4, FAKE, 3, None) == ekv.EKV_ERR_INVALID_ARG
-    assert f(None, 4, FAKE, 0, None) == ekv.EKV_ERR_INVALID_ARG
-    assert f(FAKE, 0, FAKE, 0, None) == ekv.EKV_OK
+    assert f(FAKE, 4, FAKE, 2, 0, None) == ekv.EKV_ERR_INVALID_ARG   # method
+    assert f(FAKE, 4, FAKE, 0, 128, None) == ekv.EKV_ERR_INVALID_ARG  # exponent beyond fp32 normals
+    assert f(FAKE, 4, FAKE, 1, -127, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(None, 4, FAKE, 0, 0, None) == ekv.EKV_ERR_INVALID_ARG
+    assert f(FAKE, 0, FAKE, 0, -33, None) == ekv.EKV_OK
 
 
 def test_append_validation():
@@ -274,6 +286,68 @@ def test_binding_rejects_host_tensors_and_bad_shapes():
         ekv.ekv_gather_compact_pages(kv, ids, True, ws, ws, n_pages=3)
     with pytest.raises(ValueError, match="differ"):
         ekv.ekv_decode_attention(kv, q, pt, torch.zeros((1, 5), dtype=torch.uint8), lens, 64, 0.088, out)
+
+
+def test_binding_rejects_shape_mismatches_before_any_call():
+    """Shapes the entry points take on trust -- workspace pages, output and LSE sizes, one
+    page-table row and one length per sequence, n_prompts + 1 offsets, matching head dims --
+    are checked by the binding and raise before the library is called (host tensors here:
+    a shape error is raised before the device check)."""
+    import torch
+
+    f16, f32, i32, u8 = torch.float16, torch.float32, torch.int32, torch.uint8
+    kv = ekv.paged_kv(8, 128, k_compact=torch.zeros((4, 16, 8, 128), dtype=f16),
+                      v_compact=torch.zeros((4, 16, 8, 128), dtype=u8), v_scale=torch.ones((4, 8), dtype=f32))
+    q = torch.zeros((2, 32, 128), dtype=f16)
+    pt = torch.zeros((2, 4), dtype=i32)
+    lens = torch.full((2,), 64, dtype=i32)
+    out = torch.zeros((2, 32, 128), dtype=f32)
+    lse = torch.zeros((2, 32), dtype=f32)
+    dec = ekv.ekv_decode_attention
+    bad_decode = [
+        dict(q=torch.zeros((2, 32, 64), dtype=f16), out=torch.zeros((2, 32, 64), dtype=f32)),  # head dim 64 vs 128
+        dict(page_table=torch.zeros((3, 4), dtype=i32)),     # rows != batch
+        dict(seq_lens=torch.full((3,), 64, dtype=i32)),     # lengths != batch
+        dict(out=torch.zeros((2, 32, 64), dtype=f32)),      # out smaller than q
+        dict(lse=torch.zeros((2, 16), dtype=f32)),          # lse of the wrong size
+    ]
+    for bad in bad_decode:
+        a = dict(q=q, page_table=pt, seq_lens=lens, out=out, lse=lse)
+        a.update(bad)
+        with pytest.raises(ValueError):
+            dec(kv, a["q"], a["page_table"], None, a["seq_lens"], 64, 0.088, a["out"], a["lse"])
+    with pytest.raises(ValueError, match="base_bounds"):
+        ekv.ekv_decode_attention_elastic(kv, q, pt, None, torch.zeros((2, 3), dtype=i32), True, lens, 64, 0.088,
+                                         out)
+    ids = torch.zeros(2, dtype=i32)
+    rows = torch.zeros((64, 8, 128), dtype=f16)            # a row view: 16x the pages it would claim
+    ws = torch.zeros((4, 16, 8, 128), dtype=f16)
+    with pytest.raises(ValueError, match="ws_k must be"):
+        ekv.ekv_gather_compact_pages(kv, ids, True, rows, rows)
+    with pytest.raises(ValueError, match="ws_v must be"):
+        ekv.ekv_gather_compact_pages(kv, ids, True, ws, torch.zeros((4, 16, 8, 64), dtype=f16))
+    pq = torch.zeros((32, 32, 128), dtype=f16)
+    pout = torch.zeros((32, 32, 128), dtype=f32)
+    k = torch.zeros((32, 8, 128), dtype=f16)
+    cu = torch.tensor([0, 16, 32], dtype=i32)
+    ks = torch.tensor([0, 16], dtype=i32)
+    with pytest.raises(ValueError, match="n_prompts"):
+        ekv.ekv_prefill_attention(pq, k, k, cu[:2], ks, 16, 0.088, pout)
+    with pytest.raises(ValueError, match="out must be"):
+        ekv.ekv_prefill_attention(pq, k, k, cu, ks, 16, 0.088, pout[:16])
+    with pytest.raises(ValueError, match="lse must be"):
+        ekv.ekv_prefill_attention(pq, k, k, cu, ks, 16, 0.088, pout, torch.zeros((32, 8), dtype=f32))
+    with pytest.raises(ValueError, match="head dim"):
+        ekv.ekv_prefill_attention(pq, torch.zeros((32, 8, 64), dtype=f16), torch.zeros((32, 8, 64), dtype=f16),
+                                  cu, ks, 16, 0.088, pout)
+    with pytest.raises(ValueError, match="cu_seqlens_q"):
+        ekv.ekv_prefill_paged_attention(kv, pq, cu, torch.zeros((3, 2), dtype=i32), None, 16, 0.088, pout)
+    with pytest.raises(ValueError, match="head dim"):
+        ekv.ekv_prefill_paged_attention(kv, torch.zeros((32, 32, 64), dtype=f16), cu,
+                                        torch.zeros((2, 2), dtype=i32), None, 16, 0.088,
+                                        torch.zeros((32, 32, 64), dtype=f32))
+    with pytest.raises(ValueError, match="out must be"):
+        ekv.ekv_prefill_paged_attention(kv, pq, cu, torch.zeros((2, 2), dtype=i32), None, 16, 0.088, pout[:8])
 
 
 @pytest.mark.parametrize("workload", ["decode", "prefill", "mixed", "writer", "elastic"])

@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from gpu_helpers import (TOL, DeviceCase, assert_close, assert_lse_close, dev, ekv,
                          f16_bits_equal_rne, max_abs, oracle_decode, step)
 from mixed_precision_paged_amd import synth
@@ -254,3 +255,34 @@ def test_one_long_sequence_every_plan():
         assert max_abs(o, outs[0]) <= TOL
     out16, _ = dc.decode(torch.float16)
     assert f16_bits_equal_rne(out16, outs[0])
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 2, 64)])
+@pytest.mark.parametrize("scale_exp", [-13, -26, 14])
+def test_compact_pages_with_extreme_page_scales(hq, hkv, d, scale_exp):
+    """Compact page-head scales far from the ~2^-7 of N(0,1) data: the stored codes stay and
+    the scales of sequence 0's pages (all of them), of every other page of sequence 1 and of
+    no page of sequence 2 are multiplied by 2^scale_exp (scales near 2^-20 and 2^-33 -- the
+    smallest a page of fp16 values can have -- and near 2^7).  Outputs against the oracle
+    with the bound taken relative to each sequence's largest |V| (2e-3 at max|V| = 4), under
+    the automatic plan, splits with a merge, and the balanced plan."""
+    step(f"decode extreme page scales 2^{scale_exp} hq={hq} hkv={hkv} d={d}")
+    c = synth.make_paged_case(70 + scale_exp + d, [700, 1000, 333], hq, hkv, d, compact_frac=1.0)
+    f = np.float32(2.0 ** scale_exp)
+    vs = c.v_scale.copy()
+    for b, every in ((0, 1), (1, 2)):
+        pages = c.page_table[b, :(int(c.seq_lens[b]) + 15) // 16][::every]
+        vs[pages] = vs[pages] * f  # exact: power-of-two factor of normal fp32 values
+    c.v_scale = vs
+    want, wlse = oracle_decode(c)
+    dc = DeviceCase(c)
+    vmax = np.array([np.nanmax(np.abs(oracle.decode_e4m3fn(
+        c.v_compact[c.page_table[b, :(int(c.seq_lens[b]) + 15) // 16]])) * vs[c.page_table[b, :(int(c.seq_lens[b]) + 15) // 16]][:, None, :, None])
+        for b in range(c.batch)])
+    for pps in (0, 16, ekv().DECODE_BALANCED):
+        out, lse = dc.decode(torch.float32, pages_per_split=pps)
+        assert np.all(np.isfinite(out)), pps
+        for b in range(c.batch):
+            err = np.abs(out[b].astype(np.float64) - want[b]).max()
+            assert err <= TOL * vmax[b] / 4, (pps, b, err, vmax[b])
+        assert_lse_close(lse, wlse)

@@ -10,21 +10,53 @@ from mixed_precision_paged_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("method,scale", [(0, 1.0), (1, 1.0), (2, 2.0 ** -7)])
-def test_device_e4m3_matches_oracle_table(method, scale):
-    """Every code in every byte position of a packed word (codes run 0..255 four times,
-    shifted by one each pass)."""
-    step(f"e4m3 table method {method}")
-    codes_np = np.concatenate([np.roll(np.arange(256, dtype=np.uint8), k) for k in range(4)])
-    codes = dev(codes_np)
-    out = torch.empty(codes_np.size, dtype=torch.float16, device="cuda")
-    ekv().ekv_e4m3_to_f16(codes, out, method)
-    got = out.cpu().numpy()
-    want = (oracle.E4M3FN_TABLE[codes_np] * scale).astype(np.float16)
+CODES = np.concatenate([np.roll(np.arange(256, dtype=np.uint8), k) for k in range(4)])  # every byte position
+
+
+def _device_e4m3(method, scale_exp):
+    codes = dev(CODES)
+    out = torch.empty(CODES.size, dtype=torch.float16, device="cuda")
+    ekv().ekv_e4m3_to_f16(codes, out, method, scale_exp)
+    return out.cpu().numpy()
+
+
+def _mismatches(got, scale_exp):
+    """Codes whose device value differs from the oracle table times 2^scale_exp rounded to
+    fp16 (nearest, ties to even; numpy's cast of the exact float64 product)."""
+    want = (oracle.E4M3FN_TABLE[CODES] * 2.0 ** scale_exp).astype(np.float16)
     nan = np.isnan(want)
     assert np.all(np.isnan(got[nan]))
-    bad = np.flatnonzero(got.view(np.uint16)[~nan] != want.view(np.uint16)[~nan])
-    assert bad.size == 0, [(int(codes_np[~nan][i]), float(got[~nan][i]), float(want[~nan][i])) for i in bad[:8]]
+    return np.flatnonzero(got.view(np.uint16)[~nan] != want.view(np.uint16)[~nan])
+
+
+@pytest.mark.parametrize("method", [0, 1])
+def test_device_e4m3_matches_oracle_table(method):
+    """Every code in every byte position of a packed word (codes run 0..255 four times,
+    shifted by one each pass), unscaled and at the typical page scale 2^-7."""
+    step(f"e4m3 table method {method}")
+    for scale_exp in (0, -7):
+        bad = _mismatches(_device_e4m3(method, scale_exp), scale_exp)
+        assert bad.size == 0, (scale_exp, [int(CODES[i]) for i in bad[:8]])
+
+
+def test_e4m3_expansion_over_every_page_scale_exponent():
+    """Power-of-two scales 2^-33 .. 2^7 (page-head scales of fp16 values lie in that range:
+    absmax / 448 with absmax from the smallest fp16 subnormal to 65504).  Both device paths --
+    the gather's fp32 arithmetic and the conversion instruction the decode uses -- equal the
+    oracle table times the scale rounded to fp16 (nearest, ties to even) at every exponent.
+    Below 2^-15 that rounding is not the identity (code * 2^x leaves the fp16 grid), which is
+    why the decode hands the instruction only -15..7 and applies the rest of the scale in fp32
+    (its parity at such scales: test_compact_pages_with_extreme_page_scales)."""
+    step("e4m3 expansion sweep over scale exponents -33..7")
+    for method in (0, 1):
+        for scale_exp in range(-33, 8):
+            bad = _mismatches(_device_e4m3(method, scale_exp), scale_exp)
+            assert bad.size == 0, (method, scale_exp, [int(CODES[i]) for i in bad[:8]])
+    # the exact range: every code * 2^x is an fp16 value iff x in -15..7
+    exact = [k for k in range(-33, 8)
+             if np.array_equal((oracle.E4M3FN_TABLE[CODES] * 2.0 ** k).astype(np.float16).astype(np.float64),
+                               oracle.E4M3FN_TABLE[CODES] * 2.0 ** k, equal_nan=True)]
+    assert exact == list(range(-15, 8)), exact
 
 
 def _gather_gpu(dc, ids, apply_scale, capacity=None):

@@ -3,12 +3,10 @@
 Decode: every output element against the oracle.  Gather: bit-exact on a full
 4,096-page chunk.  Prefill: sampled rows (tile boundaries, first/last rows,
 random rows) per prompt, every head, against the oracle row by row.  Mixed
-batch: one layer routed into one output tensor, decode rows fully checked,
-prefill rows sampled, and every row written by exactly its own path; the same
-for all 36 layers on request (EKV_ALL_LAYERS=1).
+batch: all 36 layers routed through one shared workspace, decode scratch and
+output tensor, each layer's workspace bit-exact, decode rows fully checked,
+prefill rows sampled, and every row written by exactly its own path.
 """
-import concurrent.futures
-import multiprocessing
 import os
 
 import numpy as np
@@ -99,105 +97,103 @@ def test_compact_prefill_32x8192_in_four_chunks():
         del out, lse, q
 
 
-def _route_layer(L, dc, two_streams=False):
-    """Route one mixed-batch layer into one output tensor: gather -> prefill into rows
-    n_decode.. (workspace reused per layer), and decode into rows 0..n_decode-1 -- on the
-    same stream, or on a second stream beside the gather + prefill."""
-    c = L.paged
-    H, D, Hq = c.num_kv_heads, c.head_dim, c.num_q_heads
-    nd = L.n_decode
-    T = int(L.cu_seqlens_q[-1])
-    out = torch.full((nd + T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
-    lse = torch.full((nd + T, Hq), float("nan"), dtype=torch.float32, device="cuda")
-    prompts = list(range(nd, nd + len(L.prompt_lens)))
-    ids = np.concatenate([c.page_table[p, :(int(c.seq_lens[p]) + 15) // 16] for p in prompts]).astype(np.int32)
-    kv_start = np.concatenate([[0], np.cumsum((L.prompt_lens + 15) // 16 * 16)[:-1]]).astype(np.int32)
-    ws_k = torch.empty((4096, 16, H, D), dtype=torch.float16, device="cuda")
-    ws_v = torch.empty_like(ws_k)
-    lens = c.seq_lens[:nd]
-    pps = ekv().ekv_decode_plan_pages_per_split(lens, H)
-    # every input on the device first, then the launches
-    ids_d, ks_d, qp, cu = dev(ids), dev(kv_start), dev(L.q_prefill), dev(L.cu_seqlens_q)
-    q_dec, lens_d = dev(L.q_decode), dev(lens)
-    pt, fl = dc.page_table[:nd].contiguous(), dc.fidelity[:nd].contiguous()
-    main = torch.cuda.current_stream()
-    side = torch.cuda.Stream() if two_streams else main
-    side.wait_stream(main)  # the inputs and the output buffers are ready
-    ekv().ekv_gather_compact_pages(dc.kv(), ids_d, True, ws_k, ws_v, stream=main)
-    ekv().ekv_prefill_attention(qp, ws_k, ws_v, cu, ks_d, int(L.prompt_lens.max()), c.sm_scale,
-                                out[nd:], lse[nd:], stream=main)
-    ekv().ekv_decode_attention(dc.kv(), q_dec, pt, fl, lens_d, int(lens.max()), c.sm_scale,
-                               out[:nd], lse[:nd], pages_per_split=pps, stream=side)
-    torch.cuda.synchronize()
-    return out.cpu().numpy(), lse.cpu().numpy(), ids, kv_start
-
-
-def _check_routed_layer(L, seed, dc=None):
-    """Route one mixed-batch layer and check it against the oracle: every decode row,
-    sampled prefill rows, and every row written by its own path."""
-    c = L.paged
-    dc = DeviceCase(c) if dc is None else dc
-    H, D = c.num_kv_heads, c.head_dim
-    nd = L.n_decode
-    lens = c.seq_lens[:nd]
-    prompts = list(range(nd, nd + len(L.prompt_lens)))
-    o, ls, ids, kv_start = _route_layer(L, dc)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ls)), "every row written by its own path"
-    want, wlse = oracle.decode_attention(L.q_decode, c.k_target, c.v_target, c.k_compact, c.v_compact,
-                                         c.v_scale, c.page_table[:nd], c.fidelity[:nd], lens, c.sm_scale)
-    assert_close(o[:nd], want, what="decode rows")
-    assert_lse_close(ls[:nd], wlse)
-    wk, wv = oracle.gather_compact_pages(c.k_compact, c.v_compact, c.v_scale, ids, True)
-    rng = np.random.default_rng(seed)
-    sample = []
-    for i in range(len(prompts)):
-        sample += [int(L.cu_seqlens_q[i]) + r for r in _sample_rows(int(L.prompt_lens[i]), rng)]
-    pw, plw = oracle.prefill_attention(L.q_prefill, wk.reshape(-1, H, D), wv.reshape(-1, H, D),
-                                       L.cu_seqlens_q, kv_start, True, c.sm_scale, rows=sample)
-    assert_close(o[nd:][sample], pw[sample], what="prefill rows")
-    assert_lse_close(ls[nd:][sample], plw[sample])
-    return float(np.abs(o[:nd] - want).max()), float(np.abs(o[nd:][sample] - pw[sample]).max())
-
-
-def test_mixed_batch_one_layer_routed():
-    """Decode rows 0..31 and prefill rows 32.. of one layer land in one output tensor; with
-    the decode on a second stream beside the gather + prefill the output is the same bits."""
-    step("fullsize mixed batch layer 0: gather -> prefill -> decode")
-    L = synth.mixed_batch_layer(0)
-    dc = DeviceCase(L.paged)
-    _check_routed_layer(L, seed=5, dc=dc)
-    step("fullsize mixed batch layer 0: decode on a second stream")
-    o1, l1, _, _ = _route_layer(L, dc)
-    o2, l2, _, _ = _route_layer(L, dc, two_streams=True)
-    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
-    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
-
-
 N_LAYERS = 36
 
 
-def test_mixed_batch_all_36_layers():
-    """Every layer of the 36-layer mixed batch (seed 5000 + layer), each routed and checked
-    as layer 0 is.  Host input generation takes about a minute per layer, so the layers are
-    generated in worker processes (no GPU use there) a few ahead of the checks; opt in with
-    EKV_ALL_LAYERS=1."""
-    if os.environ.get("EKV_ALL_LAYERS") != "1":
-        pytest.skip("36 layers of host input generation (about a minute each); set EKV_ALL_LAYERS=1")
-    workers = max(1, min(12, (os.cpu_count() or 2) - 2))
+def _route(kv, a, ws_k, ws_v, out, lse, scratch, sm_scale, side=None):
+    """One mixed-batch layer on the device: gather the fresh prompts' pages into the shared
+    workspace, causal prefill into rows n_decode.., decode into rows 0..n_decode-1 -- on one
+    stream, or with the decode on ``side`` beside the gather + prefill."""
+    nd = a["q_decode"].shape[0]
+    main = torch.cuda.current_stream()
+    dec_stream = main if side is None else side
+    if side is not None:
+        side.wait_stream(main)  # inputs and output buffers are ready
+    ekv().ekv_gather_compact_pages(kv, a["ids"], True, ws_k, ws_v, stream=main)
+    ekv().ekv_prefill_attention(a["q_prefill"], ws_k, ws_v, a["cu_seqlens_q"], a["kv_start"], a["prompt_len"],
+                                sm_scale, out[nd:], lse[nd:], stream=main)
+    ekv().ekv_decode_attention(kv, a["q_decode"], a["page_table"], a["fidelity"], a["seq_lens"], a["max_len"],
+                               sm_scale, out[:nd], lse[:nd], scratch, pages_per_split=a["pps"],
+                               stream=dec_stream)
+    if side is not None:
+        main.wait_stream(side)
+
+
+def test_mixed_batch_36_layers_one_workspace():
+    """Every layer of the 36-layer mixed batch (seed 5000 + layer) routed as a serving step
+    routes it, through ONE workspace, one decode scratch and one output tensor reused layer
+    after layer: per layer, the gathered workspace is bit-exact, every decode row and sampled
+    prefill rows match the oracle, and every row is written by its own path.  Layer 0 is
+    also routed with its decode on a second stream beside the gather + prefill (same bits).
+
+    Host input generation and the oracle (about a minute of CPU per layer) run in worker
+    processes a few layers ahead; the GPU side uploads, launches and compares."""
+    import concurrent.futures
+    import multiprocessing
+    import shutil
+
+    import mixed_layers
+
+    H, D, Hq, nd, T = 8, 128, 32, 32, 4 * 2048
+    ws_k = torch.empty((4096, 16, H, D), dtype=torch.float16, device="cuda")
+    ws_v = torch.empty_like(ws_k)
+    out = torch.empty((nd + T, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((nd + T, Hq), dtype=torch.float32, device="cuda")
+    scratch_bytes = max(ekv().ekv_decode_scratch_bytes(nd, Hq, H, D, 32768, ekv().DECODE_BALANCED),
+                        ekv().ekv_decode_scratch_bytes(nd, Hq, H, D, 32768, 0))
+    scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device="cuda")
+    workers = max(1, min(14, (os.cpu_count() or 2) - 2))
     ahead = workers + 2
-    ctx = multiprocessing.get_context("spawn")
+    spool = mixed_layers.spool_dir(ahead)
+    ex = concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=multiprocessing.get_context("spawn"))
     worst = [0.0, 0.0]
-    with concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
-        pending = {li: ex.submit(synth.mixed_batch_layer, li) for li in range(min(N_LAYERS, ahead))}
+    try:
+        pending = {li: ex.submit(mixed_layers.prepare_layer, li, spool, 5 + li)
+                   for li in range(min(N_LAYERS, ahead))}
         for li in range(N_LAYERS):
-            L = pending.pop(li).result()
+            path, layout, e = pending.pop(li).result()
             if li + ahead < N_LAYERS:
-                pending[li + ahead] = ex.submit(synth.mixed_batch_layer, li + ahead)
-            step(f"mixed batch layer {li}: gather -> prefill -> decode")
-            dec_err, pf_err = _check_routed_layer(L, seed=5 + li)
-            worst = [max(worst[0], dec_err), max(worst[1], pf_err)]
-            print(f"layer {li}: decode max-abs {dec_err:.2e}, prefill max-abs {pf_err:.2e}", flush=True)
-            del L
+                pending[li + ahead] = ex.submit(mixed_layers.prepare_layer, li + ahead, spool, 5 + li + ahead)
+            step(f"mixed batch layer {li}: upload, gather -> prefill -> decode through the shared workspace")
+            h = mixed_layers.load_layer(path, layout)
+            a = {k: dev(h[k]) for k in ("k_target", "v_target", "k_compact", "v_compact", "v_scale", "page_table",
+                                        "fidelity", "seq_lens", "q_decode", "q_prefill", "cu_seqlens_q", "ids",
+                                        "kv_start")}
+            ws_want_k, ws_want_v = dev(h["ws_k"]), dev(h["ws_v"])
+            lens = np.array(h["seq_lens"])
+            del h
+            os.unlink(path)
+            a.update(max_len=e["max_len"], prompt_len=e["prompt_len"],
+                     pps=ekv().ekv_decode_plan_pages_per_split(lens, H))
+            assert ekv().ekv_decode_scratch_bytes(nd, Hq, H, D, e["max_len"], a["pps"]) <= scratch_bytes
+            kv = ekv().paged_kv(H, D, a["k_target"], a["v_target"], a["k_compact"], a["v_compact"], a["v_scale"])
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            _route(kv, a, ws_k, ws_v, out, lse, scratch, e["sm_scale"])
+            torch.cuda.synchronize()
+            n = a["ids"].shape[0]
+            assert torch.equal(ws_k[:n].view(torch.int16), ws_want_k.view(torch.int16)), f"layer {li}: workspace K"
+            assert torch.equal(ws_v[:n].view(torch.int16), ws_want_v.view(torch.int16)), f"layer {li}: workspace V"
+            o, ls = out.cpu().numpy(), lse.cpu().numpy()
+            assert np.all(np.isfinite(o)) and np.all(np.isfinite(ls)), f"layer {li}: every row written by its path"
+            d_err = assert_close(o[:nd], e["dec"], what=f"layer {li} decode rows")
+            assert_lse_close(ls[:nd], e["dec_lse"])
+            p_err = assert_close(o[nd:][e["sample"]], e["pre"], what=f"layer {li} prefill rows")
+            assert_lse_close(ls[nd:][e["sample"]], e["pre_lse"])
+            worst = [max(worst[0], d_err), max(worst[1], p_err)]
+            print(f"layer {li}: decode max-abs {d_err:.2e}, prefill max-abs {p_err:.2e}", flush=True)
+            if li == 0:
+                step("mixed batch layer 0: decode on a second stream")
+                out2, lse2 = torch.full_like(out, float("nan")), torch.full_like(lse, float("nan"))
+                _route(kv, a, ws_k, ws_v, out2, lse2, scratch, e["sm_scale"], side=torch.cuda.Stream())
+                torch.cuda.synchronize()
+                assert torch.equal(out2.view(torch.int32), out.view(torch.int32))
+                assert torch.equal(lse2.view(torch.int32), lse.view(torch.int32))
+                del out2, lse2
+            del a, kv, ws_want_k, ws_want_v
+    finally:
+        ex.shutdown(wait=False, cancel_futures=True)
+        shutil.rmtree(spool, ignore_errors=True)
     print(f"all {N_LAYERS} layers: worst decode max-abs {worst[0]:.2e}, prefill {worst[1]:.2e}", flush=True)
 
 

@@ -54,6 +54,7 @@ extern "C" {
                                    two pages per TARGET block (elastic decode) */
 #define EKV_MAX_PREFILL_TOKENS 8192 /* [asym] route rule: prompts of at most 8,192 tokens */
 #define EKV_DECODE_BALANCED (-1)    /* decode plan: equal shares of all page-heads per workgroup */
+#define EKV_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20) /* static scratch of the allocation-free decode */
 
 typedef enum {
   EKV_OK = 0,
@@ -192,6 +193,32 @@ ekv_status ekv_decode_attention(const ekv_paged_kv* kv, const void* q, int32_t b
                                 int32_t max_seq_len, float sm_scale, void* out, ekv_dtype out_dtype,
                                 float* lse, int32_t pages_per_split, void* scratch,
                                 size_t scratch_bytes, void* stream);
+
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation): ekv_decode_attention with the same arguments except scratch,
+ * whose role is taken by a fixed device array inside the library of
+ * EKV_NOALLOC_SCRATCH_BYTES (8 MiB) per GPU, held until the process ends.
+ * Same plans, kernels and results as ekv_decode_attention (bit for bit).
+ *
+ *   A plan whose ekv_decode_scratch_bytes(...) exceeds 8 MiB returns
+ *   EKV_ERR_WORKSPACE_TOO_SMALL before any launch (the balanced plan needs
+ *   about 4.2 KB per workgroup at 4 query heads per KV head and head dim
+ *   128, so it fits 1,792 workgroups, i.e. 7 rounds; the split plan needs
+ *   batch x num_q_heads x splits x (head_dim + 2) x 4 bytes).
+ *   The call allocates and frees nothing.  The first call on a device looks
+ *   up that device's copy of the array (once); it launches on the stream's
+ *   device (the current device for a NULL stream).  Nothing in the array has
+ *   to start at zero: every partial result is written before it is read.
+ *   Calls share the array of their GPU: two calls that overlap in time on
+ *   one GPU (other streams, or other host threads without ordering) race.
+ */
+ekv_status ekv_decode_attention_noalloc(const ekv_paged_kv* kv, const void* q, int32_t batch,
+                                        int32_t num_q_heads, const int32_t* page_table, int32_t pt_stride,
+                                        const uint8_t* fidelity, const int32_t* seq_lens, int32_t max_seq_len,
+                                        float sm_scale, void* out, ekv_dtype out_dtype, float* lse,
+                                        int32_t pages_per_split, void* stream);
 
 /*
  * Elastic decode: ekv_decode_attention over pages that may also be ElasticKV

@@ -25,6 +25,7 @@ FIDELITY_COMPACT = 1
 FIDELITY_BASE = 2
 MAX_PREFILL_TOKENS = 8192
 DECODE_BALANCED = -1  # pages_per_split: equal shares of all page-heads per workgroup
+NOALLOC_SCRATCH_BYTES = 8 << 20  # static scratch of ekv_decode_attention_noalloc
 
 EKV_OK = 0
 EKV_ERR_INVALID_ARG = 1
@@ -40,7 +41,7 @@ EXPORTED = (
     "ekv_decode_plan_pages_per_split", "ekv_decode_scratch_bytes", "ekv_decode_attention",
     "ekv_decode_attention_elastic", "ekv_gather_compact_pages", "ekv_prefill_attention",
     "ekv_prefill_paged_attention", "ekv_append_tokens", "ekv_quantize_pages", "ekv_pack_base_pairs",
-    "ekv_e4m3_to_f16", "ekv_build_id",
+    "ekv_e4m3_to_f16", "ekv_decode_attention_noalloc", "ekv_build_id",
 )
 
 
@@ -69,6 +70,10 @@ _lib.ekv_decode_attention.restype = ctypes.c_int
 _lib.ekv_decode_attention.argtypes = [
     ctypes.POINTER(PagedKV), _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _f32, _vp, ctypes.c_int,
     _vp, _i32, _vp, _sz, _vp]
+_lib.ekv_decode_attention_noalloc.restype = ctypes.c_int
+_lib.ekv_decode_attention_noalloc.argtypes = [
+    ctypes.POINTER(PagedKV), _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _f32, _vp, ctypes.c_int,
+    _vp, _i32, _vp]
 _lib.ekv_decode_attention_elastic.restype = ctypes.c_int
 _lib.ekv_decode_attention_elastic.argtypes = [
     ctypes.POINTER(PagedKV), _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _f32, _vp,
@@ -251,6 +256,21 @@ def ekv_decode_attention(kv: PagedKV, q: torch.Tensor, page_table: torch.Tensor,
         int(max_seq_len), float(sm_scale), _arg(out, "out"), _dtype_code(out), _arg(lse, "lse", _F32),
         int(pages_per_split), _arg(scratch, "scratch"), scratch.numel() * scratch.element_size(),
         _stream(stream)))
+
+
+def ekv_decode_attention_noalloc(kv: PagedKV, q: torch.Tensor, page_table: torch.Tensor,
+                                 fidelity: Optional[torch.Tensor], seq_lens: torch.Tensor, max_seq_len: int,
+                                 sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                                 pages_per_split: int = 0, stream=None) -> None:
+    """ekv_decode_attention with the library's static scratch: allocates nothing (see ekv.h)."""
+    _check_decode_shapes(kv, q, page_table, seq_lens, out, lse)
+    batch, hq, _ = q.shape
+    _same_shape(page_table, fidelity, "page_table and fidelity")
+    _check(_lib.ekv_decode_attention_noalloc(
+        _kv_ref(kv), _arg(q, "q", _F16), batch, hq, _arg(page_table, "page_table", _I32),
+        int(page_table.shape[1]), _arg(fidelity, "fidelity", _U8), _arg(seq_lens, "seq_lens", _I32),
+        int(max_seq_len), float(sm_scale), _arg(out, "out"), _dtype_code(out), _arg(lse, "lse", _F32),
+        int(pages_per_split), _stream(stream)))
 
 
 def ekv_decode_attention_elastic(kv: PagedKV, q: torch.Tensor, page_table: torch.Tensor,

@@ -22,7 +22,7 @@ def _declared():
 
 def test_every_declared_function_is_exported():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(ekv._lib, n), n
     assert sorted(ekv.EXPORTED) == names
@@ -314,8 +314,9 @@ def test_binding_rejects_shape_mismatches_before_any_call():
     for bad in bad_decode:
         a = dict(q=q, page_table=pt, seq_lens=lens, out=out, lse=lse)
         a.update(bad)
-        with pytest.raises(ValueError):
-            dec(kv, a["q"], a["page_table"], None, a["seq_lens"], 64, 0.088, a["out"], a["lse"])
+        for fn in (dec, ekv.ekv_decode_attention_noalloc):
+            with pytest.raises(ValueError):
+                fn(kv, a["q"], a["page_table"], None, a["seq_lens"], 64, 0.088, a["out"], a["lse"])
     with pytest.raises(ValueError, match="base_bounds"):
         ekv.ekv_decode_attention_elastic(kv, q, pt, None, torch.zeros((2, 3), dtype=i32), True, lens, 64, 0.088,
                                          out)
@@ -361,3 +362,14 @@ def test_bench_refuses_more_than_one_gpu(workload):
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_noalloc_decode_rejects_plans_beyond_its_static_scratch():
+    """The allocation-free decode refuses, on the host and before any device call, a plan
+    whose partial results would not fit its 8 MiB static scratch."""
+    need = ekv.ekv_decode_scratch_bytes(2048, 32, 8, 128, 65536, 1)
+    assert need > ekv.NOALLOC_SCRATCH_BYTES
+    st = ekv._lib.ekv_decode_attention_noalloc(ctypes.byref(_kv()), FAKE, 2048, 32, FAKE, 4096, FAKE, FAKE,
+                                               65536, 0.088, FAKE, 0, None, 1, None)
+    assert st == ekv.EKV_ERR_WORKSPACE_TOO_SMALL
+    assert "static decode scratch" in ekv.ekv_last_error()

@@ -373,3 +373,20 @@ def test_noalloc_decode_rejects_plans_beyond_its_static_scratch():
                                                65536, 0.088, FAKE, 0, None, 1, None)
     assert st == ekv.EKV_ERR_WORKSPACE_TOO_SMALL
     assert "static decode scratch" in ekv.ekv_last_error()
+
+
+def test_bench_cpu_baseline_pool_runs_the_oracle():
+    """bench.py's CPU baseline: a spawned pool runs the unchanged oracle over (sequence, KV
+    head) tasks on inputs shared through a memory-mapped file, and reports its worker count."""
+    import sys
+
+    sys.path.insert(0, ROOT)
+    import bench
+    from mixed_precision_paged_amd import bytemodel, synth
+
+    c = synth.make_paged_case(5, [40, 100], 8, 2, 64, compact_frac=0.5)
+    ab = bytemodel.decode_bytes(c.seq_lens, c.fidelity, 8, 2, 64)
+    r = bench.cpu_decode_baseline(c, ab, 0.2)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= bench.CPU_WORKERS_MAX
+    assert "4 (sequence, KV head) tasks" in r["sample"]

@@ -104,8 +104,8 @@ typedef struct {
 int32_t ekv_abi_version(void);
 
 /* Identity of the sources this library was built from: the sha256 (hex) of
- * the .hip and .hpp files of the kernel sources and of this header, taken by
- * the build script. */
+ * the code of the .hip and .hpp kernel sources and of this header (comments
+ * and whitespace removed), taken by the build script. */
 const char* ekv_build_id(void);
 
 /* Static description of a status code. */

@@ -11,6 +11,7 @@ import concurrent.futures
 import glob
 import hashlib
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -38,13 +39,15 @@ def source_files():
 
 
 def source_hash() -> str:
-    """sha256 over the sources' names and bytes; baked into the library as ekv_build_id()."""
+    """sha256 over the sources' names and code (comments and whitespace removed, so an edit
+    of a comment does not change it); baked into the library as ekv_build_id()."""
     h = hashlib.sha256()
     for f in source_files():
-        h.update(os.path.relpath(f, ROOT).encode() + b"\0")
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-        h.update(b"\0")
+        with open(f, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(os.path.relpath(f, ROOT).encode() + b"\0" + " ".join(text.split()).encode() + b"\0")
     return h.hexdigest()
 
 

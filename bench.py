@@ -502,7 +502,7 @@ def bench_prefill(args):
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": "compact prefill: 32 fresh prompts x 8192 tokens, 32 q / 8 KV heads, "
                                "head dim 128, causal, 4,096-page workspace, 4 chunks of 8 prompts (seed 4)"},
-        "roofline": {"bound": "mfma", "kernel": "ekv_prefill_attention (prefill_ws128_kernel)",
+        "roofline": {"bound": "mfma", "kernel": "ekv_prefill_attention (prefill_pipe_kernel)",
                      "achieved": round(tflops, 1), "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_FP16_PEAK_TFLOPS, 4), "traffic": None,
                      "avg_call_us": round(p * 1e6, 1), "flops_per_call": flops},
@@ -516,7 +516,7 @@ def bench_prefill(args):
         "gather": {"avg_chunk_us": round(g * 1e6, 1), "bytes_per_chunk": rd + wr,
                    "gbps": round((rd + wr) / g / 1e9, 1), "peak_gbps": HBM_PEAK_GBPS,
                    "frac": round((rd + wr) / g / 1e9 / HBM_PEAK_GBPS, 4)},
-        "direct_paged": {"kernel": "ekv_prefill_paged_attention (prefill_ws128_kernel, paged source)",
+        "direct_paged": {"kernel": "ekv_prefill_paged_attention (prefill_pipe_kernel, paged source)",
                          "prompts_per_launch": 32, "avg_ms": round(d * 1e3, 3),
                          "tflops": round(4 * flops / d / 1e12, 1),
                          "mfma_frac": round(4 * flops / d / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),

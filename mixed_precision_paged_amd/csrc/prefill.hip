@@ -9,40 +9,42 @@
 // P.V product, accumulation is fp32.
 //
 // This is a dense QK^T / PV contraction, so it runs on the matrix cores
-// (v_mfma_f32_32x32x16_f16, gfx950).  Workgroup = 128 query rows of one
-// query head of one prompt; wavefront w owns rows [32w, 32w+32).  Per 64-key
-// tile each wavefront computes
+// (v_mfma_f32_32x32x16_f16, gfx950).  Workgroup = 32 NW query rows of one
+// query head of one prompt; wavefront w owns rows [32w, 32w+32).  Per 32-key
+// unit each wavefront computes
 //     S^T[key][q] = K . Q^T      (A = K from LDS, B = Q in registers)
 //     O^T[d][q]  += V^T . P^T    (A = V^T from LDS, B = P^T in registers)
 // so that with the 32x32 output layout every per-query quantity (running max,
 // sum, rescale factor) lives in the lane whose column is that query: lane l
 // holds column l%32 and half of its rows; a single xor-32 exchange completes a
 // column reduction.  The key order inside the P.V contraction follows the
-// S^T register layout, and V^T is read in the same order.  S of tile t + 1 is
-// computed in the same instruction stream as the softmax of tile t.
+// S^T register layout, and V^T is read in the same order.
 // Launch order: workgroups are mapped so that each XCD (8 per MI355X, each
 // with its own L2) walks a contiguous range of (prompt, KV head) groups, so
 // the K/V rows the group's query heads share stay in one L2; within a group
 // the longest (last) causal row tiles of all its query heads start first.
 //
-// Two kernels, one arithmetic (identical operands and order, so their outputs
-// agree bit for bit).  Sources: the gather workspace, or the direct route over
-// pages ("Memory-Traffic Saturation ...", section "Existing fallback:
-// mixed-type prefill"; ElasticKV section 3.2): the prompt's own page-table
-// row, TARGET pages as stored, compact pages' E4M3 values expanded while the
-// tile is staged with the scaled gather's rounding (fp16(fp32(e4m3) *
-// fp32(scale))), so both routes feed the MFMAs identical operands.
-//   prefill_ws128_kernel  head dim 128, both sources: K and V tiles go
+// Sources: the gather workspace, or the direct route over pages
+// ("Memory-Traffic Saturation ...", section "Existing fallback: mixed-type
+// prefill"; ElasticKV section 3.2): the prompt's own page-table row, TARGET
+// pages as stored, compact pages' E4M3 values expanded while the tile is
+// staged with the scaled gather's rounding (fp16(fp32(e4m3) * fp32(scale))),
+// so both routes feed the MFMAs identical operands, and a row's arithmetic
+// does not depend on the workgroup size: the two routes agree bit for bit.
+//   prefill_pipe_kernel   head dim 128, both sources: K and V tiles go
 //                         straight from memory into swizzled LDS by buffer
 //                         loads; V^T operands come from transposing LDS
-//                         reads.  Paged: wavefront w stages page w of each
-//                         64-key tile through per-page descriptors; a
-//                         compact page's codes land in a per-wavefront LDS
-//                         area and are expanded into the V tile before the
-//                         barrier that publishes it.
+//                         reads; a three-stage pipeline over 32-key units
+//                         (described at the kernel).  Paged: wavefront w
+//                         stages page w of each 64-key tile through per-page
+//                         descriptors; a compact page's codes land in a
+//                         per-wavefront LDS area and are expanded into the V
+//                         tile before the barrier that publishes it.
 //   prefill_kernel        head dim 64, both sources: K and V staged through
 //                         registers; V^T transposed with byte permutes on its
-//                         way into padded LDS tiles.
+//                         way into padded LDS tiles; one 64-key tile per step.
+#include <utility>
+
 #include "ekv_device.hpp"
 #include "ekv_internal.hpp"
 
@@ -405,7 +407,7 @@ __device__ bool stage_page_meta(const PrefillParams& p, int prompt, int g, int L
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, int n_mtiles) {
-  static_assert(D == 64, "head dim 128 runs prefill_ws128_kernel");
+  static_assert(D == 64, "head dim 128 runs prefill_pipe_kernel");
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   // K of tiles i + 1 (computing S ahead) and i + 2 (being stored), V of
@@ -715,7 +717,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
 //   4 (i % 4), so lane j receives V[key0 + k][d0 + j] for k = 0..3: four keys
 //   of one d, the A-operand layout of O^T = V^T P^T.
 constexpr int kWsD = 128;
-constexpr int kWsWaves = 4;  // measured: 4 wavefronts (128 rows) beat 8 (256 rows) by 5%
+// Wavefronts per workgroup (32 query rows each).  Paged source: 4, one page
+// of each 64-key tile per wavefront.  Workspace source: 8 for prompts of at
+// least kLongPrompt tokens (a staged tile serves 256 rows: 3-4% faster at
+// 8 x 8192), 4 below (more workgroups: 11% faster at 32 x 512).
+constexpr int kPagedWaves = 4;
+constexpr int kLongPrompt = 2048;
 __host__ __device__ inline bool paged_route(const PrefillParams& p) { return p.page_table != nullptr; }
 
 
@@ -726,29 +733,59 @@ __device__ __forceinline__ uint2 lds_tr16(const f16* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// NW wavefronts, 32 NW query rows per workgroup, sharing every staged tile.
-// PAGED: keys and values come from the prompt's pages (4 wavefronts: each
-// stages the K and V of one page of the tile).
+// Calls f(integral_constant<int, S>) for S = 0, 1, ...: a fully unrolled
+// sequence whose step index is a compile-time constant in each call.
+template <typename F, int... S>
+__device__ __forceinline__ void unroll_steps(F&& f, std::integer_sequence<int, S...>) {
+  (f(std::integral_constant<int, S>{}), ...);
+}
+
+// Head dim 128, both sources.  NW wavefronts of 32 query rows each share the
+// staged K and V tiles; two wavefronts per SIMD (at most 256 VGPRs each).
+// The loop runs over 32-key units u (half a 64-key tile) as a three-stage
+// software pipeline: body u computes S(u + 2) = K Q^T and O += V(u)^T P(u)
+// on the matrix cores while the vector ALUs take the exponentials of
+// S(u + 1); none of the three depends on another.  The running max of a
+// unit is found in the body that produces its scores, against the running
+// max before it (deferred rescale: it moves only when the unit's max
+// exceeds it by more than tau); the factor exp2(m_old - m_new) scales l at
+// the start of the next body and O after that body's P.V products, so
+// every row sees the usual online-softmax recurrence with one rescale per
+// unit at most.  P is rounded to fp16 for the P.V MFMAs and l sums those
+// same fp16 values (v_dot2_f32_f16), so the normalisation divides by
+// exactly the weights that multiplied V.
+// Issue budget: one v_exp_f32 costs a wavefront about 8.5 clocks of issue
+// and a plain VALU operation about 4.7, with no overlap between the two;
+// a 32x32x16 MFMA keeps the matrix core busy 32 clocks.  A body has 16
+// MFMAs, 16 exponentials and about 60 other VALU operations per
+// wavefront, so the two wavefronts of a SIMD must interleave closely to
+// keep the matrix cores fed: the steps of a full tile are fixed in order
+// (see full_tile) with one exponential per MFMA.
 template <int NW, bool PAGED>
-__global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillParams p, int n_mtiles) {
+__global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(PrefillParams p, int n_mtiles) {
+  constexpr int RB = 1;  // 32-row blocks per wavefront (the loops below allow more)
   constexpr int D = kWsD;
-  constexpr int QUADS = 16 / NW;  // K (and V) row quads each wavefront stages per tile
+  constexpr int WR = 32 * RB;   // query rows per wavefront (RB 32-row blocks)
+  constexpr int QUADS = 16 / NW;
   static_assert(!PAGED || QUADS * 4 == kPage, "paged staging: one page per wavefront");
-  constexpr int KS = D / 16;  // k-steps of 16 over the head dim
-  constexpr int DB = D / 32;  // 32-row blocks of O^T
-  constexpr int TILE = kN * D;  // halves per K or V tile
-  // K of tiles t + 1 (computing S ahead) and t + 2 (being staged), V of
-  // tiles t (P.V) and t + 1 (being staged)
-  __shared__ __attribute__((aligned(1024))) f16 kbuf[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) f16 vbuf[2 * TILE];
-  // paged source: E4M3 codes of the compact page each wavefront stages, and
-  // the prompt's page metadata
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = kN * D;
+  // Four separate tile buffers: with the buffer known at compile time in the
+  // main loop, the compiler can tell that a tile's LDS reads do not touch
+  // the buffers the next tiles are being loaded into, and does not wait for
+  // those loads before the reads.
+  __shared__ __attribute__((aligned(1024))) f16 kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) f16 kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) f16 vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) f16 vb1[TILE];
+  auto kbuf_of = [&](int b) -> f16* { return b ? kb1 : kb0; };
+  auto vbuf_of = [&](int b) -> f16* { return b ? vb1 : vb0; };
   __shared__ __attribute__((aligned(16))) uint8_t vcodes[PAGED ? NW * kPage * D : 16];
   __shared__ __attribute__((aligned(16))) int s_meta[PAGED ? kMaxPromptPages : 4];
   __shared__ __attribute__((aligned(16))) float s_scale[PAGED ? kMaxPromptPages : 4];
   __shared__ int s_bad;
 
-  // XCD-aware work mapping (as in prefill_kernel).
   const WorkItem wi = work_item(p, n_mtiles);
   const int prompt = wi.prompt, h = wi.h, mt = wi.mt;
   const int G = p.num_q_heads / p.num_kv_heads;
@@ -758,7 +795,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
   const int q1 = p.cu_seqlens_q[prompt + 1];
   if (q0 < 0 || q1 < q0 || q1 > p.q_rows) return;  // rows not addressable: nothing to write
   const int L = q1 - q0;
-  const int m0 = mt * 32 * NW;
+  const int m0 = mt * WR * NW;
   const int kv0 = PAGED ? 0 : p.kv_start[prompt];
   const bool ok = PAGED ? (L <= p.max_len && L <= kMaxPromptPages * kPage &&
                            (int64_t)L <= (int64_t)p.pt_stride * kPage)
@@ -772,27 +809,20 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int r0 = m0 + 32 * wave;
-  const int qpos = r0 + col;
-  const int64_t qrow = (int64_t)q0 + qpos;
+  const int r0 = m0 + WR * wave;
   const int64_t hq_row = (int64_t)p.num_q_heads * D;
-  const int n_end = p.causal ? min(L, m0 + 32 * NW) : L;
+  const int n_end = p.causal ? min(L, m0 + WR * NW) : L;
   const int n_tiles = (n_end + kN - 1) / kN;
-  const int n_w = p.causal ? min(n_tiles, (r0 + 31) / kN + 1) : n_tiles;
   const uint32_t rowb = (uint32_t)p.num_kv_heads * D * 2u;
-  const uint32_t rowb8 = (uint32_t)p.num_kv_heads * D;  // E4M3 row (paged source)
+  const uint32_t rowb8 = (uint32_t)p.num_kv_heads * D;
 
   if constexpr (PAGED) {
-    // page ids, kinds and scales of pages 0 .. 4 n_tiles - 1; an out-of-pool
-    // id or unknown flag marks the row tile bad (its rows are written as NaN)
     if (!stage_page_meta(p, prompt, g, L, 4 * n_tiles, s_meta, s_scale, &s_bad)) {
-      write_nan_rows<D>(p, q0, m0, min(L, m0 + 32 * NW), h);
+      write_nan_rows<D>(p, q0, m0, min(L, m0 + WR * NW), h);
       return;
     }
   }
 
-  // workspace source: descriptors over this prompt's K/V rows of KV head g
-  // (rows past the prompt read as zeros); paged source: pool bases at head g
   const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2u;
   const char* kbase = reinterpret_cast<const char*>(PAGED ? p.k_target : p.k) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
   const char* vbase = reinterpret_cast<const char*>(PAGED ? p.v_target : p.v) + ((int64_t)kv0 * p.num_kv_heads + g) * D * 2;
@@ -801,8 +831,6 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, span, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, span, kBufferFlags);
 
-  // staging: row quad j of this wavefront = tile rows 4 (QUADS wave + j) .. + 3
-  // (paged: rows 4 j .. + 3 of the wavefront's page; offsets within the page)
   uint32_t kso[QUADS], vso[QUADS];
 #pragma unroll
   for (int j = 0; j < QUADS; ++j) {
@@ -811,7 +839,6 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
     kso[j] = (uint32_t)rs * rowb + 16u * (uint32_t)(pc ^ (r & 15));
     vso[j] = (uint32_t)rs * rowb + 16u * (uint32_t)(pc ^ (4 * (r & 3)));
   }
-  // paged compact V: lane l takes 16 codes of page row 8 c + l / 8 (c = 0, 1)
   uint32_t cso[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) cso[c] = (uint32_t)(8 * c + (lane >> 3)) * rowb8 + 16u * (uint32_t)(lane & 7);
@@ -823,16 +850,13 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
       const __amdgpu_buffer_rsrc_t kd = __builtin_amdgcn_make_buffer_rsrc(
           (void*)base, (short)0, (kPage - 1) * rowb + D * 2u, kBufferFlags);
 #pragma unroll
-      for (int j = 0; j < QUADS; ++j) lds_dma16(kd, &kbuf[b * TILE + 4 * (QUADS * wave + j) * D], kso[j]);
+      for (int j = 0; j < QUADS; ++j) lds_dma16(kd, kbuf_of(b) + 4 * (QUADS * wave + j) * D, kso[j]);
     } else {
       const uint32_t to = (uint32_t)(t * kN) * rowb;
 #pragma unroll
-      for (int j = 0; j < QUADS; ++j) lds_dma16(kr, &kbuf[b * TILE + 4 * (QUADS * wave + j) * D], kso[j] + to);
+      for (int j = 0; j < QUADS; ++j) lds_dma16(kr, kbuf_of(b) + 4 * (QUADS * wave + j) * D, kso[j] + to);
     }
   };
-  // Paged: a TARGET page's values go straight to the tile; a compact page's
-  // codes go to this wavefront's staging area and are expanded by put_v.
-  // The descriptors end at the prompt's last row, so later rows read zeros.
   auto stage_v = [&](int t, int b) {
     if constexpr (PAGED) {
       const int pj = 4 * t + wave;
@@ -849,17 +873,14 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
         const __amdgpu_buffer_rsrc_t vd = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(vbase + phys * kPage * rowb), (short)0, valid ? (valid - 1) * rowb + D * 2u : 0u, kBufferFlags);
 #pragma unroll
-        for (int j = 0; j < QUADS; ++j) lds_dma16(vd, &vbuf[b * TILE + 4 * (QUADS * wave + j) * D], vso[j]);
+        for (int j = 0; j < QUADS; ++j) lds_dma16(vd, vbuf_of(b) + 4 * (QUADS * wave + j) * D, vso[j]);
       }
     } else {
       const uint32_t to = (uint32_t)(t * kN) * rowb;
 #pragma unroll
-      for (int j = 0; j < QUADS; ++j) lds_dma16(vr, &vbuf[b * TILE + 4 * (QUADS * wave + j) * D], vso[j] + to);
+      for (int j = 0; j < QUADS; ++j) lds_dma16(vr, vbuf_of(b) + 4 * (QUADS * wave + j) * D, vso[j] + to);
     }
   };
-  // Paged compact page (after its codes have landed): lane l expands the 32
-  // codes of page row l / 4, d 32 (l % 4) .. + 31, with the gather's rounding
-  // (fp16(fp32(code) * fp32(scale))) into the swizzled V tile.
   auto put_v = [&](int t, int b) {
     if constexpr (PAGED) {
       const int pj = 4 * t + wave;
@@ -870,7 +891,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
         const uint4 c0 = *reinterpret_cast<const uint4*>(cs);
         const uint4 c1 = *reinterpret_cast<const uint4*>(cs + 16);
         const int R = kPage * wave + r;
-        f16* row = &vbuf[b * TILE + R * D];
+        f16* row = vbuf_of(b) + R * D;
         const int sw = 4 * (R & 3);
         *reinterpret_cast<uint4*>(row + 8 * ((4 * sg + 0) ^ sw)) = expand8(make_uint2(c0.x, c0.y), sc);
         *reinterpret_cast<uint4*>(row + 8 * ((4 * sg + 1) ^ sw)) = expand8(make_uint2(c0.z, c0.w), sc);
@@ -880,13 +901,9 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
     }
   };
 
-  // QK^T A operand: K row kb*32 + col, chunk 2 ks + half at chunk (2 ks + half) ^ (col % 16)
   uint32_t kro[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) kro[ks] = (uint32_t)col * D + 8u * (uint32_t)((2 * ks + half) ^ (col & 15));
-  // V^T A operand (transposing reads): lane i = l % 16 of group q16 = l / 16
-  // addresses key row 4 (q16 / 2) + i / 4 (+ 16 kk, + 8 for the high keys)
-  // at d = 32 db + 16 (q16 % 2) + 4 (i % 4)
   uint32_t vro[DB];
   {
     const int i = lane & 15, q16 = lane >> 4;
@@ -898,140 +915,361 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_ws128_kernel(PrefillPar
     }
   }
 
-  // Q^T operand: lane holds Q[qpos][16ks + 8half .. +8] for each k-step.
-  f16x8 qb[KS];
+  // Q^T operands of both row blocks: query r0 + 32 rb + col
+  f16x8 qb[RB][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (qpos < L) {
-      const uint4 x = *reinterpret_cast<const uint4*>(p.q + qrow * hq_row + (int64_t)h * D + 16 * ks + 8 * half);
-      qb[ks] = __builtin_bit_cast(f16x8, x);
-    } else {
-      qb[ks] = f16x8{};
+  for (int rb = 0; rb < RB; ++rb) {
+    const int qpos = r0 + 32 * rb + col;
+    const int64_t qrow = (int64_t)q0 + qpos;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (qpos < L) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p.q + qrow * hq_row + (int64_t)h * D + 16 * ks + 8 * half);
+        qb[rb][ks] = __builtin_bit_cast(f16x8, x);
+      } else {
+        qb[rb][ks] = f16x8{};
+      }
     }
   }
-  f32x16 oacc[DB];
+  f32x16 oacc[RB][DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m = kNegBig, l = 0.f;
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[rb][i] = f32x16{};
+  // Running softmax state.  Body u (below) takes the exponentials of unit
+  // u + 1 with m = m(u + 1) and finds m(u + 2) into mn; al = alpha(u + 1) =
+  // exp2(m(u) - m(u + 1)) scales l at the body's start and O after the
+  // body's P(u) products (mv: whether any row of the wavefront moved).
+  float m[RB], l[RB], al[RB], mn[RB], aln[RB];
+  bool mv = false, mvn = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegBig;
+    l[rb] = 0.f;
+    al[rb] = 1.f;
+    mn[rb] = kNegBig;
+    aln[rb] = 1.f;
+  }
 
-  auto qk_block = [&](f32x16& sacc, int b, int kb) {
-    sacc = f32x16{};
-    const f16* kp = &kbuf[b * TILE + kb * 32 * D];
+  // Unit u = keys 32 u .. 32 u + 31 = half u % 2 of tile u / 2.
+  // S(u) of both row blocks; each K operand read feeds two MFMAs.
+  auto qk_unit = [&](f32x16 (&s)[RB], int u) {
+    const f16* kp = kbuf_of((u >> 1) & 1) + (u & 1) * 32 * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const f16x8 a = *reinterpret_cast<const f16x8*>(kp + kro[ks]);
-      sacc = mfma32(a, qb[ks], sacc);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32(a, qb[rb][ks], ks == 0 ? f32x16{} : s[rb]);
     }
   };
-  auto mask_tile = [&](f32x16 (&sacc)[2], int n0) {
+  auto unit_needs_mask = [&](int u) { return (p.causal && 32 * u + 31 > r0) || (32 * u + 32 > L); };
+  // Called under a wave-uniform branch; the empty asm keeps the compiler from
+  // turning that branch into selects executed for every unit.
+  auto mask_unit = [&](f32x16 (&s)[RB], int u) {
+    asm volatile("");
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int rb = 0; rb < RB; ++rb) {
+      const int qpos = r0 + 32 * rb + col;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = n0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+        const int key = 32 * u + 8 * (r / 4) + 4 * half + (r % 4);
         const bool vis = key < L && (!p.causal || key <= qpos);
-        sacc[kb][r] = vis ? sacc[kb][r] : -__builtin_inff();
+        s[rb][r] = vis ? s[rb][r] : -__builtin_inff();
       }
     }
   };
-  auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int kb_buf, int vb_buf) {
-    qk_block(nxt[0], kb_buf, 0);
-    float mx = -__builtin_inff();
+  // Running max of a unit against mref, the running max before it: it moves
+  // only when the unit's max exceeds mref by more than tau.  xm: the
+  // lane's max, ym: the max of the other half-wavefront's lane (same row).
+  // Writes the new max and the factor exp2(mref - new) (exactly 1 where
+  // the max stays); returns whether any row of the wavefront moved.
+  auto new_max = [&](const float (&xm)[RB], const float (&ym)[RB], const float (&mref)[RB], float (&mout)[RB],
+                     float (&aout)[RB]) {
+    bool moved = false;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
-    mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
-    const float mnew = (mx > m + kTau) ? mx : m;
-    if (__ballot(mnew != m)) {
-      const float a = fast_exp2(m - mnew);
-      l *= a;
-#pragma unroll
-      for (int i = 0; i < DB; ++i) oacc[i] *= a;
-      m = mnew;
+    for (int rb = 0; rb < RB; ++rb) {
+      const float x = fmaxf(xm[rb], ym[rb]) * p.scale_log2;
+      const float mnew = (x > mref[rb] + kTau) ? x : mref[rb];
+      moved |= mnew != mref[rb];
+      aout[rb] = fast_exp2(mref[rb] - mnew);
+      mout[rb] = mnew;
     }
-    qk_block(nxt[1], kb_buf, 1);
-    const f16* vt = &vbuf[vb_buf * TILE];
+    return __ballot(moved) != 0;
+  };
+  auto unit_max = [&](const f32x16 (&s)[RB], const float (&mref)[RB], float (&mout)[RB], float (&aout)[RB]) {
+    float xm[RB], ym[RB];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      f16x8 pb;
+    for (int rb = 0; rb < RB; ++rb) {
+      float x = s[rb][0];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float pv = fast_exp2(__builtin_fmaf(cur[kk / 2][8 * (kk % 2) + r], p.scale_log2, -m));
-        l += pv;
-        pb[r] = (f16)pv;
+      for (int r = 1; r < 16; ++r) x = fmaxf(x, s[rb][r]);
+      xm[rb] = x;
+      ym[rb] = shfl_xor(x, 32);
+    }
+    return new_max(xm, ym, mref, mout, aout);
+  };
+  // P(u) = exp2(S(u) scale_log2 - m) as the fp16 B operands of the P.V
+  // MFMAs; l sums those same fp16 values in fp32, a pair per v_dot2_f32_f16,
+  // so the normalisation divides by exactly the weights that multiplied V.
+  auto unit_exps = [&](const f32x16 (&s)[RB], f16x8 (&pn)[RB][2]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[rb][e], p.scale_log2, -m[rb]));
+        const float p1 = fast_exp2(__builtin_fmaf(s[rb][e + 1], p.scale_log2, -m[rb]));
+        const f16x2 pr = {(f16)p0, (f16)p1};
+        l[rb] = __builtin_amdgcn_fdot2(pr, f16x2{(f16)1.0f, (f16)1.0f}, l[rb], false);
+        pn[rb][e / 8][e % 8] = pr[0];
+        pn[rb][e / 8][e % 8 + 1] = pr[1];
       }
+    }
+  };
+  // O += V(u)^T P(u); each V^T operand feeds RB MFMAs
+  auto pv_unit = [&](const f16x8 (&pb)[RB][2], int u) {
+    const f16* vt = vbuf_of((u >> 1) & 1);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int kk = 2 * (u & 1) + k2;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        // keys 16 kk + 4 half' + 0..3 (lo) and + 8 (hi) of d 32 db + col
         const uint2 lo = lds_tr16(vt + vro[db] + 16 * kk * D);
         const uint2 hi = lds_tr16(vt + vro[db] + (16 * kk + 8) * D);
-        const uint4 a4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        oacc[db] = mfma32(__builtin_bit_cast(f16x8, a4), pb, oacc[db]);
+        const f16x8 a = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32(a, pb[rb][k2], oacc[rb][db]);
       }
     }
   };
+  // Marks P as used here: keeps its exponentials in the body whose matrix
+  // work hides them instead of letting them sink towards their first use.
+  auto pin_p = [&](const f16x8 (&pb)[RB][2]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) asm volatile("" ::"v"(pb[rb][k2]));
+  };
+  auto scale_l = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l[rb] *= al[rb];
+  };
+  auto rescale_o = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[rb][i] *= al[rb];
+  };
+  // end of a body: the next body's max and factor become current
+  auto rotate = [&](bool have_next) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (have_next) m[rb] = mn[rb];
+      al[rb] = have_next ? aln[rb] : 1.f;
+    }
+    mv = have_next && mvn;
+  };
 
-  // Prologue: K(0), V(0), K(1) staged; then S(0).
+  // units this wavefront computes: up to its last row's diagonal and the
+  // prompt's end (none if all its rows lie past the prompt)
+  const int n_u = r0 >= L ? 0 : min(p.causal ? (r0 + WR - 1) / 32 + 1 : 2 * n_tiles, (L + 31) / 32);
+  // Prologue: K(0), V(0), K(1) staged; S(0), its max, P(0); S(1) and its max.
   stage_k(0, 0);
   stage_v(0, 0);
   if (n_tiles > 1) stage_k(1, 1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's tile loads have landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   put_v(0, 0);
   __syncthreads();
-  f32x16 sA[2], sB[2];
-  qk_block(sA[0], 0, 0);
-  qk_block(sA[1], 0, 1);
-  // The first iteration stages K(2) into buffer 0: every wavefront must have
-  // read K(0) from it first (later reuses are ordered by the per-tile barrier).
+  f32x16 sA[RB], sB[RB];
+  f16x8 pA[RB][2], pB[RB][2];
+  if (n_u > 0) {
+    qk_unit(sB, 0);
+    if (unit_needs_mask(0)) mask_unit(sB, 0);
+    unit_max(sB, m, mn, aln);  // l and O are still zero: no rescale
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) m[rb] = mn[rb];
+    unit_exps(sB, pA);
+    bool have1 = false;
+    if (n_u > 1) {
+      qk_unit(sA, 1);
+      if (unit_needs_mask(1)) mask_unit(sA, 1);
+      mvn = unit_max(sA, m, mn, aln);
+      have1 = true;
+    }
+    rotate(have1);
+  }
   __syncthreads();
 
-  // Iteration t: K(t+2) and V(t+1) stream into LDS while S(t+1) runs on the
-  // matrix cores and the softmax of S(t) on the vector ALUs, then O += V(t)
-  // P(t); the staged tiles land in the buffers freed by K(t) and V(t-1).
-#define EKV_WS_STEP(CUR, NXT)                                                                   \
-  {                                                                                             \
-    if (it + 2 < n_tiles) stage_k(it + 2, it & 1);                                              \
-    if (it + 1 < n_tiles) stage_v(it + 1, (it + 1) & 1);                                        \
-    if (it < n_w) {                                                                             \
-      if ((p.causal && it * kN + kN - 1 > r0) || (it * kN + kN > L)) mask_tile(CUR, it * kN);   \
-      step(CUR, NXT, (it + 1) & 1, it & 1);                                                     \
-    }                                                                                           \
-    __builtin_amdgcn_s_waitcnt(0x0F70);                                                         \
-    if (it + 1 < n_tiles) put_v(it + 1, (it + 1) & 1);                                          \
-    __syncthreads();                                                                            \
-    if (++it >= n_tiles) break;                                                                 \
-  }
-  for (int it = 0; it < n_tiles;) {
-    EKV_WS_STEP(sA, sB)
-    EKV_WS_STEP(sB, sA)
-  }
-#undef EKV_WS_STEP
-
-  // normalize and store rows of this lane's column
-  l += shfl_xor(l, 32);
-  if (qpos >= L) return;
-  const float inv = 1.0f / l;
-  const int64_t obase = qrow * hq_row + (int64_t)h * D;
+  // A tile whose two bodies u = 2 t and 2 t + 1 both have all their parts
+  // runs as one explicitly ordered sequence of 32 steps (sched_barrier
+  // fences keep the order).  Body b, step j issues
+  //   j < 8:  the MFMA(s) of k-step j of S(u + 2)             (operand: K)
+  //   j >= 8: the MFMA(s) of O += V(u)^T P(u) for (k2, db) =
+  //           ((j - 8) / 4, (j - 8) % 4)                      (operand: V^T)
+  // the LDS read of the operand of step j + kAhead, the exponential of
+  // score j of S(u + 1) (l scaled first at j 0, fp16 pairs packed at odd
+  // j), and from j 10 on the running max of S(u + 2): the lane max (j 10,
+  // 11; the cross-half exchange goes through LDS) and the new max and
+  // factor (j 14).  One transcendental and a few plain VALU operations per
+  // MFMA keep the vector ALUs under the matrix cores' time.  Only the first
+  // kAhead reads after the tile's barrier can stall the matrix cores.
+  constexpr int kAhead = 3;
+  // The tile parity (which of the two K and V buffers) is a compile-time
+  // constant, so every LDS operand address is a fixed register plus an
+  // immediate offset.
+  auto full_tile = [&](int t, auto parity) {
+    constexpr int par = decltype(parity)::value;
+    const f16* kt = (par ^ 1) ? kb1 : kb0;  // K(t + 1): S(2t + 2) (keys 0..31), S(2t + 3)
+    const f16* vt = par ? vb1 : vb0;        // V(t): P(2t) (kk 0, 1), P(2t + 1) (kk 2, 3)
+    auto operand = [&](int s) -> f16x8 {
+      const int b = s >> 4, j = s & 15;
+      if (j < 8) return *reinterpret_cast<const f16x8*>(kt + b * 32 * D + kro[j]);
+      const int kk = 2 * b + ((j - 8) >> 2), db = (j - 8) & 3;
+      const uint2 lo = lds_tr16(vt + vro[db] + 16 * kk * D);
+      const uint2 hi = lds_tr16(vt + vro[db] + (16 * kk + 8) * D);
+      return __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
+    f16x8 ring[kAhead + 1];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+    for (int s = 0; s < kAhead; ++s) ring[s] = operand(s);
+    float xm[RB], ym[RB], pe[RB];
+    auto step = [&](auto step_index) {
+      constexpr int s = decltype(step_index)::value;
+      constexpr int b = s >> 4, j = s & 15;
+      f32x16 (&sn)[RB] = b == 0 ? sB : sA;    // S(u + 2), produced
+      f32x16 (&sc)[RB] = b == 0 ? sA : sB;    // S(u + 1), exponentials
+      f16x8 (&pc)[RB][2] = b == 0 ? pA : pB;  // P(u), consumed by P.V
+      f16x8 (&pn)[RB][2] = b == 0 ? pB : pA;  // P(u + 1), produced
+      if constexpr (s + kAhead < 32) ring[(s + kAhead) % (kAhead + 1)] = operand(s + kAhead);
+      const f16x8 a = ring[s % (kAhead + 1)];
+      if constexpr (j < 8) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int d = 32 * db + 8 * rb + 4 * half;
-      const float o0 = oacc[db][4 * rb + 0] * inv, o1 = oacc[db][4 * rb + 1] * inv;
-      const float o2 = oacc[db][4 * rb + 2] * inv, o3 = oacc[db][4 * rb + 3] * inv;
-      if (p.out_f32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + d) = f32x4{o0, o1, o2, o3};
+        for (int rb = 0; rb < RB; ++rb) sn[rb] = mfma32(a, qb[rb][j], j == 0 ? f32x16{} : sn[rb]);
       } else {
-        f16x2 a, b;
-        a.x = (f16)o0; a.y = (f16)o1; b.x = (f16)o2; b.y = (f16)o3;
-        *reinterpret_cast<uint2*>(static_cast<f16*>(p.out) + obase + d) = make_uint2(bits(a), bits(b));
+        constexpr int k2 = (j - 8) >> 2, db = (j - 8) & 3;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32(a, pc[rb][k2], oacc[rb][db]);
+      }
+      if constexpr (j == 0) scale_l();
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float pv = fast_exp2(__builtin_fmaf(sc[rb][j], p.scale_log2, -m[rb]));
+        if constexpr ((j & 1) == 0) {
+          pe[rb] = pv;
+        } else {
+          const f16x2 pr = {(f16)pe[rb], (f16)pv};
+          l[rb] = __builtin_amdgcn_fdot2(pr, f16x2{(f16)1.0f, (f16)1.0f}, l[rb], false);
+          pn[rb][j / 8][(j % 8) - 1] = pr[0];
+          pn[rb][j / 8][j % 8] = pr[1];
+        }
+      }
+      if constexpr (j == 10) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float x = sn[rb][0];
+#pragma unroll
+          for (int r = 1; r < 8; ++r) x = fmaxf(x, sn[rb][r]);
+          xm[rb] = x;
+        }
+      } else if constexpr (j == 11) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float x = xm[rb];
+#pragma unroll
+          for (int r = 8; r < 16; ++r) x = fmaxf(x, sn[rb][r]);
+          xm[rb] = x;
+          ym[rb] = shfl_xor(x, 32);
+        }
+      } else if constexpr (j == 14) {
+        mvn = new_max(xm, ym, m, mn, aln);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (j == 7) {
+        // the first eight exponentials stay ahead of the mask branch
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(l[rb]), "v"(pn[rb][0]));
+        if (unit_needs_mask(2 * t + b + 2)) mask_unit(sn, 2 * t + b + 2);
+      } else if constexpr (j == 15) {
+        pin_p(pn);
+        if (mv) rescale_o();
+        rotate(true);
+      }
+    };
+    unroll_steps(step, std::make_integer_sequence<int, 32>{});
+  };
+  // The same for the last units of the wavefront (some parts absent).
+#define EKV_PIPE_TAIL(U, SC, SN, PC, PN)                                  \
+  if ((U) < n_u) {                                                        \
+    scale_l();                                                            \
+    if ((U) + 1 < n_u) unit_exps(SC, PN);                                 \
+    const bool have_next = (U) + 2 < n_u;                                 \
+    if (have_next) {                                                      \
+      qk_unit(SN, (U) + 2);                                               \
+      if (unit_needs_mask((U) + 2)) mask_unit(SN, (U) + 2);               \
+      mvn = unit_max(SN, m, mn, aln);                                     \
+    }                                                                     \
+    pv_unit(PC, (U));                                                     \
+    if (mv) rescale_o();                                                  \
+    rotate(have_next);                                                    \
+  }
+  // Tiles whose two bodies are both complete form the main loop; every tile
+  // (either loop) stages K(t + 2) and V(t + 1) and ends at the barrier.
+  const int n_full = max(0, min(n_tiles, (n_u - 2) / 2));
+  int it = 0;
+  auto main_tile = [&](int t, auto parity) {
+    constexpr int par = decltype(parity)::value;
+    if (t + 2 < n_tiles) stage_k(t + 2, par);
+    if (t + 1 < n_tiles) stage_v(t + 1, par ^ 1);
+    full_tile(t, parity);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (t + 1 < n_tiles) put_v(t + 1, par ^ 1);
+    __syncthreads();
+  };
+  for (; it + 1 < n_full; it += 2) {
+    main_tile(it, std::integral_constant<int, 0>{});
+    main_tile(it + 1, std::integral_constant<int, 1>{});
+  }
+  if (it < n_full) {
+    main_tile(it, std::integral_constant<int, 0>{});
+    ++it;
+  }
+  for (; it < n_tiles; ++it) {
+    if (it + 2 < n_tiles) stage_k(it + 2, it & 1);
+    if (it + 1 < n_tiles) stage_v(it + 1, (it + 1) & 1);
+    EKV_PIPE_TAIL(2 * it, sA, sB, pA, pB)
+    EKV_PIPE_TAIL(2 * it + 1, sB, sA, pB, pA)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (it + 1 < n_tiles) put_v(it + 1, (it + 1) & 1);
+    __syncthreads();
+  }
+#undef EKV_PIPE_TAIL
+
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    l[rb] += shfl_xor(l[rb], 32);
+    const int qpos = r0 + 32 * rb + col;
+    if (qpos >= L) continue;
+    const int64_t qrow = (int64_t)q0 + qpos;
+    const float inv = 1.0f / l[rb];
+    const int64_t obase = qrow * hq_row + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = 32 * db + 8 * rq + 4 * half;
+        const float o0 = oacc[rb][db][4 * rq + 0] * inv, o1 = oacc[rb][db][4 * rq + 1] * inv;
+        const float o2 = oacc[rb][db][4 * rq + 2] * inv, o3 = oacc[rb][db][4 * rq + 3] * inv;
+        if (p.out_f32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + d) = f32x4{o0, o1, o2, o3};
+        } else {
+          f16x2 a, b;
+          a.x = (f16)o0; a.y = (f16)o1; b.x = (f16)o2; b.y = (f16)o3;
+          *reinterpret_cast<uint2*>(static_cast<f16*>(p.out) + obase + d) = make_uint2(bits(a), bits(b));
+        }
       }
     }
+    if (p.lse && half == 0) p.lse[qrow * p.num_q_heads + h] = (m[rb] + log2f(l[rb])) * kLn2;
   }
-  if (p.lse && half == 0) p.lse[qrow * p.num_q_heads + h] = (m + log2f(l)) * kLn2;
 }
-
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
@@ -1042,13 +1280,12 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const bool paged = paged_route(p);
   if (paged && p.max_len > kMaxPromptPages * kPage) return hipErrorInvalidValue;
   if (p.head_dim == kWsD) {
-    constexpr int NW = kWsWaves;
-    const int n_mt = (p.max_len + 32 * NW - 1) / (32 * NW);
-    const int64_t nb = (int64_t)n_mt * p.num_q_heads * p.n_prompts;
-    if (paged)
-      hipLaunchKernelGGL((prefill_ws128_kernel<NW, true>), dim3((unsigned)nb), dim3(NW * kWave), 0, stream, p, n_mt);
-    else
-      hipLaunchKernelGGL((prefill_ws128_kernel<NW, false>), dim3((unsigned)nb), dim3(NW * kWave), 0, stream, p, n_mt);
+    const int nw = paged ? kPagedWaves : p.max_len >= kLongPrompt ? 8 : 4;
+    const int n_mt = (p.max_len + 32 * nw - 1) / (32 * nw);
+    const dim3 g((unsigned)((int64_t)n_mt * p.num_q_heads * p.n_prompts)), blk(nw * kWave);
+    if (paged) hipLaunchKernelGGL((prefill_pipe_kernel<kPagedWaves, true>), g, blk, 0, stream, p, n_mt);
+    else if (nw == 8) hipLaunchKernelGGL((prefill_pipe_kernel<8, false>), g, blk, 0, stream, p, n_mt);
+    else hipLaunchKernelGGL((prefill_pipe_kernel<4, false>), g, blk, 0, stream, p, n_mt);
     return hipGetLastError();
   }
   if (p.head_dim == 64) {

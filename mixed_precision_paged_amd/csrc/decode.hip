@@ -58,6 +58,10 @@ constexpr int kMaxSplitPages = 512;   // pages per split (metadata staged in LDS
 constexpr int kBalancedRound = 256;     // balanced plan: workgroups per round (one per CU)
 constexpr int kBalancedMaxPages = 512;  // balanced plan: pages per range (LDS stage)
 constexpr int kBalancedWaves = 8;       // balanced plan: wavefronts per workgroup
+constexpr int kNonTemporal = 2;      // buffer-load cache policy bit: non-temporal (streamed once)
+constexpr int kKAux = 0;              // cache policy of K page loads
+constexpr int kVAux = kNonTemporal;   // cache policy of V page loads
+constexpr int kBaseKAux = 0;          // cache policy of BASE K page loads
 constexpr int kSlots = 2;             // register page buffers per wavefront (pages in flight + 1)
 constexpr int kMinWaves = 2;          // occupancy bound (wavefronts per SIMD) for G*D < 1024
 constexpr int kExpLo = -15;           // code * 2^x is exact in fp16 for every E4M3 code iff
@@ -90,7 +94,7 @@ struct Slot {
 // byte per K element: a lane's 8 K values of a k-step are 8 bytes at `kqoff8`,
 // loaded into the low half of r.k[kb] and expanded before the MFMA; their V
 // bytes take the compact path's byte layout.
-template <int D, bool HAS_BASE>
+template <int D, bool HAS_BASE, int KAUX, int VAUX>
 __device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* kbase,
                                           const char* vbase, uint32_t kbytes, uint32_t vbytes,
                                           uint32_t kqoff, uint32_t kqoff8, uint32_t voff16, uint32_t voff8,
@@ -100,13 +104,13 @@ __device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* 
   if (HAS_BASE && kind == 2) {
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
-      const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(kr, kqoff8 + 32u * kb, 0, 0);
+      const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(kr, kqoff8 + 32u * kb, 0, kBaseKAux);
       r.k[kb] = __builtin_bit_cast(f16x8, u32x4{a.x, a.y, 0u, 0u});
     }
   } else {
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb)
-      r.k[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, kqoff + 64u * kb, 0, 0));
+      r.k[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, kqoff + 64u * kb, 0, KAUX));
   }
   if constexpr (HAS_BASE) {
     // Same load sequence for every kind (and for no page: range-0
@@ -122,7 +126,7 @@ __device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (HW == 2) {
-          const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(vr, voff8, i * vrow, 0);
+          const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(vr, voff8, i * vrow, VAUX);
           r.v[i][0] = a.x; r.v[i][1] = a.y;
         } else {
           r.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff8, i * vrow, 0);
@@ -132,7 +136,7 @@ __device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (HW == 2) {
-          const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(vr, voff16, i * krow, 0);
+          const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(vr, voff16, i * krow, VAUX);
           r.v[i][0] = a.x; r.v[i][1] = a.y;
         } else {
           r.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff16, i * krow, 0);
@@ -142,7 +146,7 @@ __device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (HW == 2) {
-        const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(hr, voff16 + 8u, i * krow, 0);
+        const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(hr, voff16 + 8u, i * krow, VAUX);
         r.v[i][2] = b.x; r.v[i][3] = b.y;
       } else {
         r.v[i][1] = __builtin_amdgcn_raw_buffer_load_b32(hr, voff16 + 4u, i * krow, 0);
@@ -152,7 +156,7 @@ __device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (D == 128) {
-        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vr, voff16, i * krow, 0);
+        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vr, voff16, i * krow, VAUX);
         r.v[i][0] = y.x; r.v[i][1] = y.y; r.v[i][2] = y.z; r.v[i][3] = y.w;
       } else {
         const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(vr, voff16, i * krow, 0);
@@ -163,7 +167,7 @@ __device__ __forceinline__ void load_page(PageRegs<D>& r, int kind, const char* 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (D == 128) {
-        const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(vr, voff8, i * vrow, 0);
+        const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(vr, voff8, i * vrow, VAUX);
         r.v[i][0] = y.x; r.v[i][1] = y.y; r.v[i][2] = 0u; r.v[i][3] = 0u;
       } else {
         r.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff8, i * vrow, 0);
@@ -351,7 +355,7 @@ struct PieceSmem {
 // take the pages round-robin and leave their (max, sum, unnormalized acc) and
 // bad-page flags in sm, published by a barrier.  The caller must not reuse sm
 // before every wavefront has read what it needs (a barrier).
-template <int D, int G, int MODE, int NW, class SM>
+template <int D, int G, int MODE, int NW, int KAUX, int VAUX, class SM>
 __device__ __forceinline__ void run_piece(const DecodeParams& p, SM& sm, int b, int g, int len,
                                           int pbeg, int pend, int lane, int wave) {
   constexpr int kThreads = NW * kWave;
@@ -441,7 +445,7 @@ __device__ __forceinline__ void run_piece(const DecodeParams& p, SM& sm, int b, 
       vbytes = 0u;
     }
     sl.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sm.scale[pq - pbeg])));
-    load_page<D, HAS_BASE>(sl.r, sl.kind, kb, vb, kbytes, vbytes, kqoff, kqoff8, voff16, voff8, krow, vrow);
+    load_page<D, HAS_BASE, KAUX, VAUX>(sl.r, sl.kind, kb, vb, kbytes, vbytes, kqoff, kqoff8, voff16, voff8, krow, vrow);
   };
   // kSlots register page buffers: pages pg+4 .. pg+4(kSlots-1) load while page pg
   // computes.  Slots are named variables (never an indexed array) so they stay
@@ -588,7 +592,7 @@ __global__ __launch_bounds__(NW * kWave, kMinWaves) void decode_splitk_kernel(De
     return;
   }
   const int pend = min(pbeg + p.pages_per_split, npages);
-  run_piece<D, G, MODE, NW>(p, sm, b, g, len, pbeg, pend, lane, wave);
+  run_piece<D, G, MODE, NW, kKAux, kVAux>(p, sm, b, g, len, pbeg, pend, lane, wave);
   if constexpr (DIRECT) write_rows<D, G, NW>(p, sm, b, g);
   else write_partial<D, G, NW>(p, sm, ((int64_t)(b * p.num_kv_heads + g) * p.n_splits + split));
 }
@@ -672,7 +676,7 @@ __global__ __launch_bounds__(kBalancedWaves * kWave, kMinWaves) void decode_bala
     const int64_t seg = (int64_t)H * s_pref[b] + (int64_t)g * np;
     const int pend = (int)(min(w1, seg + np) - seg);
     const int len = min(max(p.seq_lens[b], 0), p.max_seq_len);
-    run_piece<D, G, MODE, NW>(p, sm, b, g, len, page, pend, lane, wave);
+    run_piece<D, G, MODE, NW, kKAux, kVAux>(p, sm, b, g, len, page, pend, lane, wave);
     if (page == 0 && pend == np) write_rows<D, G, NW>(p, sm, b, g);
     else write_partial<D, G, NW>(p, sm, 2 * (int64_t)i + (q == w0 ? 0 : 1));
     q = seg + pend;

@@ -122,15 +122,20 @@ int32_t ekv_decode_plan_pages_per_split(const int32_t* seq_lens_host, int32_t ba
   if (maxp == 0) return 16;
   if (total * 10 >= maxp * batch * 9) {  // lengths within ~10% of the longest: splits
     const int32_t pps = ekv::decode_auto_pages_per_split(batch, num_kv_heads, (int32_t)maxp);
-    // ... unless the split plan launches between one and two rounds of its
-    // 4-wavefront workgroups (768 resident on the 256-CU part at 3 per CU):
-    // its last round would run part-empty, and equal shares do better there
-    // (measured: batch 128 x 8192 tokens 584 vs 666 us, 32 x 32768 592 vs
-    // 619, 128 x 2048 163 vs 174; outside that window the splits win)
+    // ... unless the split plan launches more than one round of its
+    // 4-wavefront workgroups (768 resident on the 256-CU part at 3 per CU),
+    // or only a few long sequences.  Equal shares measured ahead there, the
+    // splits everywhere else (us, splits vs equal shares, V loads
+    // non-temporal): one to two rounds, batch 128 x 8192 tokens 528 both,
+    // 32 x 32768 526 both, 128 x 2048 148 vs 146; more rounds, 64 x 32768
+    // 1068 vs 1032, 128 x 32768 2075 vs 2008; at most 32 (sequence, KV head)
+    // groups of 2,048+ pages, 1 x 32768 37.8 vs 32.2, 4 x 32768 70.2 vs 68.1;
+    // one round or less, 64 x 8192 261 vs 269, 16 x 32768 264 vs 269.
     const int64_t groups = (int64_t)batch * num_kv_heads;
     const int64_t wgs = groups * ((maxp + pps - 1) / pps);
     const bool eight_wave = groups <= 256 && wgs == groups;
-    if (!eight_wave && wgs > kSplitRound && wgs <= 2 * kSplitRound && batch <= ekv::kDecodeMaxBalancedBatch)
+    if (batch <= ekv::kDecodeMaxBalancedBatch &&
+        ((!eight_wave && wgs > kSplitRound) || (groups <= 32 && maxp >= 2048)))
       return EKV_DECODE_BALANCED;
     return pps;
   }

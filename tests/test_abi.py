@@ -128,11 +128,12 @@ def test_split_plan_from_host_lengths():
     assert ragged % 4 == 0 and 16 <= ragged <= 512 and abs(ragged - pages * 8 / 4096) <= 4
     assert ekv.ekv_decode_plan_pages_per_split([], 8) == 16
     assert ekv.ekv_decode_plan_pages_per_split([0, 0], 8) == 16
-    # near-equal lengths whose split plan would launch one to two rounds of 4-wavefront
-    # workgroups (768 < n <= 1,536) get equal shares instead; outside that window, splits
-    for b, ctx in ((128, 8192), (32, 32768), (128, 2048)):
+    # near-equal lengths whose split plan would launch more than one round of 4-wavefront
+    # workgroups (n > 768), or at most 32 (sequence, KV head) groups of 2,048+ pages, get
+    # equal shares instead; otherwise splits
+    for b, ctx in ((128, 8192), (32, 32768), (128, 2048), (64, 32768), (128, 32768), (1, 32768), (4, 32768)):
         assert ekv.ekv_decode_plan_pages_per_split(np.full(b, ctx), 8) == ekv.DECODE_BALANCED, (b, ctx)
-    for b, ctx, pps in ((64, 8192, 512), (64, 32768, 512), (128, 32768, 512), (16, 8192, 128), (1, 32768, 32)):
+    for b, ctx, pps in ((64, 8192, 512), (16, 32768, 512), (16, 8192, 128), (1, 8192, 16), (64, 2048, 128)):
         assert ekv.ekv_decode_plan_pages_per_split(np.full(b, ctx), 8) == pps, (b, ctx)
 
 

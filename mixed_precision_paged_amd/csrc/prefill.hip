@@ -35,8 +35,9 @@
 //                         straight from memory into swizzled LDS by buffer
 //                         loads; V^T operands come from transposing LDS
 //                         reads; a three-stage pipeline over 32-key units
-//                         (described at the kernel).  Paged: wavefront w
-//                         stages page w of each 64-key tile through per-page
+//                         (described at the kernel).  Paged: each wavefront
+//                         stages one page (4 wavefronts) or half a page (8)
+//                         of each 64-key tile through per-page
 //                         descriptors; a compact page's codes land in a
 //                         per-wavefront LDS area and are expanded into the V
 //                         tile before the barrier that publishes it.
@@ -717,11 +718,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
 //   4 (i % 4), so lane j receives V[key0 + k][d0 + j] for k = 0..3: four keys
 //   of one d, the A-operand layout of O^T = V^T P^T.
 constexpr int kWsD = 128;
-// Wavefronts per workgroup (32 query rows each).  Paged source: 4, one page
-// of each 64-key tile per wavefront.  Workspace source: 8 for prompts of at
-// least kLongPrompt tokens (a staged tile serves 256 rows: 3-4% faster at
-// 8 x 8192), 4 below (more workgroups: 11% faster at 32 x 512).
-constexpr int kPagedWaves = 4;
+// Wavefronts per workgroup (32 query rows each), either source: 8 for
+// prompts of at least kLongPrompt tokens (a staged tile serves 256 rows:
+// 3-4% faster at 8 x 8192), 4 below (more workgroups: 11% faster at
+// 32 x 512).  Paged source: a wavefront stages one page of each 64-key tile
+// at 4 wavefronts, half a page at 8.
 constexpr int kLongPrompt = 2048;
 __host__ __device__ inline bool paged_route(const PrefillParams& p) { return p.page_table != nullptr; }
 
@@ -767,7 +768,11 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   constexpr int D = kWsD;
   constexpr int WR = 32 * RB;   // query rows per wavefront (RB 32-row blocks)
   constexpr int QUADS = 16 / NW;
-  static_assert(!PAGED || QUADS * 4 == kPage, "paged staging: one page per wavefront");
+  // paged source: a 64-key tile is 4 pages; each wavefront stages RPW rows
+  // of page wave / PPW (a whole page at 4 wavefronts, half a page at 8)
+  constexpr int PPW = NW / 4;
+  constexpr int RPW = kPage / PPW;
+  static_assert(!PAGED || NW == 4 || NW == 8, "paged staging: a page or half a page per wavefront");
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = kN * D;
@@ -781,7 +786,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   __shared__ __attribute__((aligned(1024))) f16 vb1[TILE];
   auto kbuf_of = [&](int b) -> f16* { return b ? kb1 : kb0; };
   auto vbuf_of = [&](int b) -> f16* { return b ? vb1 : vb0; };
-  __shared__ __attribute__((aligned(16))) uint8_t vcodes[PAGED ? NW * kPage * D : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t vcodes[PAGED ? NW * RPW * D : 16];
   __shared__ __attribute__((aligned(16))) int s_meta[PAGED ? kMaxPromptPages : 4];
   __shared__ __attribute__((aligned(16))) float s_scale[PAGED ? kMaxPromptPages : 4];
   __shared__ int s_bad;
@@ -845,7 +850,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   auto page_meta = [&](int j) { return __builtin_amdgcn_readfirstlane(s_meta[j]); };
   auto stage_k = [&](int t, int b) {
     if constexpr (PAGED) {
-      const int meta = page_meta(4 * t + wave);
+      const int meta = page_meta(4 * t + wave / PPW);
       const char* base = ((meta & 1) ? kcbase : kbase) + (int64_t)(meta >> 1) * kPage * rowb;
       const __amdgpu_buffer_rsrc_t kd = __builtin_amdgcn_make_buffer_rsrc(
           (void*)base, (short)0, (kPage - 1) * rowb + D * 2u, kBufferFlags);
@@ -859,7 +864,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   };
   auto stage_v = [&](int t, int b) {
     if constexpr (PAGED) {
-      const int pj = 4 * t + wave;
+      const int pj = 4 * t + wave / PPW;
       const int meta = page_meta(pj);
       const uint32_t valid = (uint32_t)min(max(L - kPage * pj, 0), kPage);
       const int64_t phys = meta >> 1;
@@ -867,8 +872,9 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
         const __amdgpu_buffer_rsrc_t vd = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(vcbase + phys * kPage * rowb8), (short)0, valid ? (valid - 1) * rowb8 + D : 0u, kBufferFlags);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          lds_dma16(vd, reinterpret_cast<f16*>(&vcodes[wave * kPage * D + 1024 * c]), cso[c]);
+        for (int c = 0; c < 2 / PPW; ++c)  // 1 KiB = 8 code rows per load
+          lds_dma16(vd, reinterpret_cast<f16*>(&vcodes[wave * RPW * D + 1024 * c]),
+                    cso[PPW == 1 ? c : (wave & 1)]);
       } else {
         const __amdgpu_buffer_rsrc_t vd = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(vbase + phys * kPage * rowb), (short)0, valid ? (valid - 1) * rowb + D * 2u : 0u, kBufferFlags);
@@ -883,20 +889,23 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   };
   auto put_v = [&](int t, int b) {
     if constexpr (PAGED) {
-      const int pj = 4 * t + wave;
+      const int pj = 4 * t + wave / PPW;
       if (page_meta(pj) & 1) {
+        // lane l expands CPL codes of staged row l / SEGS, d CPL (l % SEGS) ..
+        constexpr int SEGS = kWave / RPW, CPL = D / SEGS;
         const float sc = rfl(s_scale[pj]);
-        const int r = lane >> 2, sg = lane & 3;
-        const uint8_t* cs = &vcodes[wave * kPage * D + r * D + 32 * sg];
-        const uint4 c0 = *reinterpret_cast<const uint4*>(cs);
-        const uint4 c1 = *reinterpret_cast<const uint4*>(cs + 16);
-        const int R = kPage * wave + r;
+        const int r = lane / SEGS, sg = lane % SEGS;
+        const uint8_t* cs = &vcodes[wave * RPW * D + r * D + CPL * sg];
+        const int R = RPW * wave + r;
         f16* row = vbuf_of(b) + R * D;
         const int sw = 4 * (R & 3);
-        *reinterpret_cast<uint4*>(row + 8 * ((4 * sg + 0) ^ sw)) = expand8(make_uint2(c0.x, c0.y), sc);
-        *reinterpret_cast<uint4*>(row + 8 * ((4 * sg + 1) ^ sw)) = expand8(make_uint2(c0.z, c0.w), sc);
-        *reinterpret_cast<uint4*>(row + 8 * ((4 * sg + 2) ^ sw)) = expand8(make_uint2(c1.x, c1.y), sc);
-        *reinterpret_cast<uint4*>(row + 8 * ((4 * sg + 3) ^ sw)) = expand8(make_uint2(c1.z, c1.w), sc);
+#pragma unroll
+        for (int h = 0; h < CPL / 16; ++h) {
+          const uint4 c = *reinterpret_cast<const uint4*>(cs + 16 * h);
+          const int ch = (CPL / 8) * sg + 2 * h;
+          *reinterpret_cast<uint4*>(row + 8 * ((ch + 0) ^ sw)) = expand8(make_uint2(c.x, c.y), sc);
+          *reinterpret_cast<uint4*>(row + 8 * ((ch + 1) ^ sw)) = expand8(make_uint2(c.z, c.w), sc);
+        }
       }
     }
   };
@@ -1280,10 +1289,11 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const bool paged = paged_route(p);
   if (paged && p.max_len > kMaxPromptPages * kPage) return hipErrorInvalidValue;
   if (p.head_dim == kWsD) {
-    const int nw = paged ? kPagedWaves : p.max_len >= kLongPrompt ? 8 : 4;
+    const int nw = p.max_len >= kLongPrompt ? 8 : 4;
     const int n_mt = (p.max_len + 32 * nw - 1) / (32 * nw);
     const dim3 g((unsigned)((int64_t)n_mt * p.num_q_heads * p.n_prompts)), blk(nw * kWave);
-    if (paged) hipLaunchKernelGGL((prefill_pipe_kernel<kPagedWaves, true>), g, blk, 0, stream, p, n_mt);
+    if (paged && nw == 8) hipLaunchKernelGGL((prefill_pipe_kernel<8, true>), g, blk, 0, stream, p, n_mt);
+    else if (paged) hipLaunchKernelGGL((prefill_pipe_kernel<4, true>), g, blk, 0, stream, p, n_mt);
     else if (nw == 8) hipLaunchKernelGGL((prefill_pipe_kernel<8, false>), g, blk, 0, stream, p, n_mt);
     else hipLaunchKernelGGL((prefill_pipe_kernel<4, false>), g, blk, 0, stream, p, n_mt);
     return hipGetLastError();

@@ -118,3 +118,47 @@ def test_bad_page_id_marks_its_row_tiles_nan():
     want, wlse = _oracle(c, pc.cu_seqlens_q, rows=np.r_[0:128, 400:460])
     assert_close(out[:128], want[:128])
     assert_close(out[400:], want[400:])
+
+
+def test_long_ragged_compact_prompts_bit_equal_to_gather_route():
+    """From 2,048 tokens both routes run 256-row workgroups (the direct route stages half a
+    page of each key tile per wavefront); ragged lengths leave partial pages, key tiles and
+    row tiles at the ends, and the 1- and 17-token prompts share the launch."""
+    step("paged prefill long ragged compact prompts (256-row workgroups)")
+    lens = [2100, 1, 700, 2048, 17, 2305]
+    pc = synth.make_prefill_case(440, lens, 8, 2, 128)
+    c = pc.paged
+    out, lse = _paged(c, pc.cu_seqlens_q, max(lens))
+    g_out, g_lse = _gather_route(pc)
+    assert np.array_equal(out.view(np.uint32), g_out.view(np.uint32)), "differs from the gather route"
+    assert np.array_equal(lse.view(np.uint32), g_lse.view(np.uint32))
+    want, wlse = _oracle(c, pc.cu_seqlens_q)
+    assert_close(out, want)
+    assert_lse_close(lse, wlse)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_ragged_mixed_fidelity_prompts_match_oracle(causal):
+    step(f"paged prefill long ragged mixed fidelity causal={causal}")
+    lens = [2305, 1, 2048, 999]
+    case = synth.make_paged_case(450, lens, 8, 2, 128, compact_frac=0.5, query_rows=int(sum(lens)))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    out, lse = _paged(case, cu, max(lens), causal=causal)
+    want, wlse = _oracle(case, cu, causal=causal)
+    assert_close(out, want)
+    assert_lse_close(lse, wlse)
+
+
+def test_bad_page_id_in_a_long_prompt_marks_its_256_row_tiles_nan():
+    step("paged prefill bad page id, 256-row workgroups")
+    lens = [2100, 60]
+    pc = synth.make_prefill_case(460, lens, 8, 2, 128)
+    c = pc.paged
+    pt = c.page_table.copy()
+    pt[0, 40] = c.k_compact.shape[0] + 5          # keys 640..655 of prompt 0: row tiles 2.. read it
+    out, lse = _paged(c, pc.cu_seqlens_q, max(lens), pt=pt)
+    assert np.all(np.isnan(out[512:2100])) and np.all(np.isnan(lse[512:2100]))
+    assert np.all(np.isfinite(out[:512])) and np.all(np.isfinite(out[2100:]))
+    want, wlse = _oracle(c, pc.cu_seqlens_q, rows=np.r_[0:512, 2100:2160])
+    assert_close(out[:512], want[:512])
+    assert_close(out[2100:], want[2100:])

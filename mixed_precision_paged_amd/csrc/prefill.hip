@@ -41,6 +41,9 @@
 //                         descriptors; a compact page's codes land in a
 //                         per-wavefront LDS area and are expanded into the V
 //                         tile before the barrier that publishes it.
+//                         Query rows (8 wavefronts) and fp16 output rows
+//                         pass through LDS so that every load and store
+//                         instruction moves whole 256-byte rows.
 //   prefill_kernel        head dim 64, both sources: K and V staged through
 //                         registers; V^T transposed with byte permutes on its
 //                         way into padded LDS tiles; one 64-key tile per step.
@@ -790,6 +793,10 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   __shared__ __attribute__((aligned(16))) int s_meta[PAGED ? kMaxPromptPages : 4];
   __shared__ __attribute__((aligned(16))) float s_scale[PAGED ? kMaxPromptPages : 4];
   __shared__ int s_bad;
+  // At 8 wavefronts (one workgroup per CU) each wavefront's 32 query rows
+  // come in through this area: 8 KiB per wavefront, 64 KiB in all.
+  constexpr bool QST = NW == 8;
+  __shared__ __attribute__((aligned(1024))) f16 qst[QST ? NW * 32 * kWsD : 8];
 
   const WorkItem wi = work_item(p, n_mtiles);
   const int prompt = wi.prompt, h = wi.h, mt = wi.mt;
@@ -926,17 +933,37 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
 
   // Q^T operands of both row blocks: query r0 + 32 rb + col
   f16x8 qb[RB][KS];
+  f16* const qw = qst + (QST ? wave * 32 * D : 0);
+  if constexpr (QST) {
+    // Whole 256-byte rows by LDS-DMA, four rows per instruction, so each
+    // load covers full cache lines (the operand layout below would touch 32
+    // rows per instruction); lane l of load i fetches chunk (l % 16) ^ (row
+    // % 16) of row 4 i + l / 16, so chunk k of a row sits at position k ^
+    // (row % 16) and the operand reads below are bank-conflict free.  The
+    // descriptor ends at the prompt's last row: rows past it arrive as zeros.
+    static_assert(RB == 1, "one 32-row block per wavefront");
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.q + (int64_t)q0 * hq_row + (int64_t)h * D), (short)0,
+        (uint32_t)(L - 1) * (uint32_t)hq_row * 2u + D * 2u, kBufferFlags);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int qpos = r0 + 32 * rb + col;
-    const int64_t qrow = (int64_t)q0 + qpos;
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const uint32_t c = (uint32_t)((lane & 15) ^ (r & 15));
+      lds_dma16(qr, qw + i * 512, (uint32_t)(r0 + r) * (uint32_t)hq_row * 2u + 16u * c);
+    }
+  } else {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (qpos < L) {
-        const uint4 x = *reinterpret_cast<const uint4*>(p.q + qrow * hq_row + (int64_t)h * D + 16 * ks + 8 * half);
-        qb[rb][ks] = __builtin_bit_cast(f16x8, x);
-      } else {
-        qb[rb][ks] = f16x8{};
+    for (int rb = 0; rb < RB; ++rb) {
+      const int qpos = r0 + 32 * rb + col;
+      const int64_t qrow = (int64_t)q0 + qpos;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (qpos < L) {
+          const uint4 x = *reinterpret_cast<const uint4*>(p.q + qrow * hq_row + (int64_t)h * D + 16 * ks + 8 * half);
+          qb[rb][ks] = __builtin_bit_cast(f16x8, x);
+        } else {
+          qb[rb][ks] = f16x8{};
+        }
       }
     }
   }
@@ -1088,6 +1115,11 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   __builtin_amdgcn_s_waitcnt(0x0F70);
   put_v(0, 0);
   __syncthreads();
+  if constexpr (QST) {  // each wavefront reads back only what its own loads wrote
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qb[0][ks] = *reinterpret_cast<const f16x8*>(qw + col * D + 8 * ((2 * ks + half) ^ (col & 15)));
+  }
   f32x16 sA[RB], sB[RB];
   f16x8 pA[RB][2], pB[RB][2];
   if (n_u > 0) {
@@ -1252,6 +1284,42 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   }
 #undef EKV_PIPE_TAIL
 
+  if (!p.out_f32) {
+    // fp16 rows go out through LDS so that each store instruction writes
+    // four whole 256-byte rows (written from the accumulator layout, each
+    // store instruction would touch 32 rows, 16 bytes each, and the
+    // epilogue took 2.6x as long).  The tile buffers are free after the last
+    // barrier: 8 KiB per wavefront, 16-byte chunks XOR-swizzled by row; each
+    // wavefront reads back only its own rows.  fp32 rows keep direct stores.
+    static_assert(RB == 1, "one 32-row block per wavefront");
+    f16* ost = ((wave >> 1) == 0 ? kb0 : (wave >> 1) == 1 ? kb1 : (wave >> 1) == 2 ? vb0 : vb1) + (wave & 1) * 32 * D;
+    l[0] += shfl_xor(l[0], 32);
+    const int qpos = r0 + col;
+    const float inv = 1.0f / l[0];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        f16x2 a, b;
+        a.x = (f16)(oacc[0][db][4 * rq + 0] * inv); a.y = (f16)(oacc[0][db][4 * rq + 1] * inv);
+        b.x = (f16)(oacc[0][db][4 * rq + 2] * inv); b.y = (f16)(oacc[0][db][4 * rq + 3] * inv);
+        *reinterpret_cast<uint2*>(ost + col * D + 8 * ((4 * db + rq) ^ (col & 15)) + 4 * half) =
+            make_uint2(bits(a), bits(b));
+      }
+    }
+    if (p.lse && half == 0 && qpos < L)
+      p.lse[((int64_t)q0 + qpos) * p.num_q_heads + h] = (m[0] + log2f(l[0])) * kLn2;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int c = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const uint4 v = *reinterpret_cast<const uint4*>(ost + r * D + 8 * (c ^ (r & 15)));
+      if (r0 + r < L)
+        *reinterpret_cast<uint4*>(static_cast<f16*>(p.out) + ((int64_t)q0 + r0 + r) * hq_row + (int64_t)h * D + 8 * c) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     l[rb] += shfl_xor(l[rb], 32);

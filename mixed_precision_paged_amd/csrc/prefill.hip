@@ -988,14 +988,19 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   }
 
   // Unit u = keys 32 u .. 32 u + 31 = half u % 2 of tile u / 2.
-  // S(u) of both row blocks; each K operand read feeds two MFMAs.
+  // S(u) (prologue and last units; RB row blocks share each K operand).
+  // All eight K operands are read before the first MFMA, so the chain waits
+  // for one LDS latency instead of one per k-step.
   auto qk_unit = [&](f32x16 (&s)[RB], int u) {
     const f16* kp = kbuf_of((u >> 1) & 1) + (u & 1) * 32 * D;
+    f16x8 a[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const f16x8*>(kp + kro[ks]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const f16x8 a = *reinterpret_cast<const f16x8*>(kp + kro[ks]);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32(a, qb[rb][ks], ks == 0 ? f32x16{} : s[rb]);
+      for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32(a[ks], qb[rb][ks], ks == 0 ? f32x16{} : s[rb]);
     }
   };
   auto unit_needs_mask = [&](int u) { return (p.causal && 32 * u + 31 > r0) || (32 * u + 32 > L); };

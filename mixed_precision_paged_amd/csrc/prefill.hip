@@ -940,16 +940,19 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
     // rows per instruction); lane l of load i fetches chunk (l % 16) ^ (row
     // % 16) of row 4 i + l / 16, so chunk k of a row sits at position k ^
     // (row % 16) and the operand reads below are bank-conflict free.  The
-    // descriptor ends at the prompt's last row: rows past it arrive as zeros.
+    // descriptor starts at this wavefront's first row (offsets stay within
+    // 32 rows for any prompt length) and ends at the prompt's last row:
+    // rows past it arrive as zeros.
     static_assert(RB == 1, "one 32-row block per wavefront");
+    const int qrows = max(0, min(L - r0, WR));
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.q + (int64_t)q0 * hq_row + (int64_t)h * D), (short)0,
-        (uint32_t)(L - 1) * (uint32_t)hq_row * 2u + D * 2u, kBufferFlags);
+        (void*)(p.q + ((int64_t)q0 + r0) * hq_row + (int64_t)h * D), (short)0,
+        qrows ? (uint32_t)(qrows - 1) * (uint32_t)hq_row * 2u + D * 2u : 0u, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 4 * i + (lane >> 4);
       const uint32_t c = (uint32_t)((lane & 15) ^ (r & 15));
-      lds_dma16(qr, qw + i * 512, (uint32_t)(r0 + r) * (uint32_t)hq_row * 2u + 16u * c);
+      lds_dma16(qr, qw + i * 512, (uint32_t)r * (uint32_t)hq_row * 2u + 16u * c);
     }
   } else {
 #pragma unroll

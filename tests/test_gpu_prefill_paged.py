@@ -162,3 +162,43 @@ def test_bad_page_id_in_a_long_prompt_marks_its_256_row_tiles_nan():
     want, wlse = _oracle(c, pc.cu_seqlens_q, rows=np.r_[0:512, 2100:2160])
     assert_close(out[:512], want[:512])
     assert_close(out[2100:], want[2100:])
+
+
+@pytest.mark.parametrize("route", ["paged", "gather"])
+def test_long_ragged_fp16_rows_are_rne_of_fp32_and_spare_rows_untouched(route):
+    """From 2,048 tokens the fp16 output rows leave through LDS four whole rows per store: each
+    must equal the RNE of the fp32 row, and query rows past the last prompt (present in q and
+    out but in no prompt) must keep what they held, LSE included."""
+    step(f"prefill fp16 rows through LDS, 256-row workgroups, {route} route")
+    lens = [2100, 1, 700, 2305]
+    pc = synth.make_prefill_case(470, lens, 8, 2, 128)
+    c = pc.paged
+    dc = DeviceCase(c)
+    T, spare = int(pc.cu_seqlens_q[-1]), 40
+    q = torch.cat([dc.q, torch.randn((spare, c.num_q_heads, c.head_dim), device="cuda").half()])
+    cu = dev(pc.cu_seqlens_q)
+    if route == "gather":
+        ids, kv_start = pc.chunk_pages(list(range(len(lens))))
+        ws_k = torch.empty((len(ids), 16, c.num_kv_heads, c.head_dim), dtype=torch.float16, device="cuda")
+        ws_v = torch.empty_like(ws_k)
+        ekv().ekv_gather_compact_pages(dc.kv(), dev(ids), True, ws_k, ws_v)
+    outs = {}
+    for dtype in (torch.float32, torch.float16):
+        out = torch.full((T + spare, c.num_q_heads, c.head_dim), 7.0, dtype=dtype, device="cuda")
+        lse = torch.full((T + spare, c.num_q_heads), 7.0, dtype=torch.float32, device="cuda")
+        if route == "paged":
+            ekv().ekv_prefill_paged_attention(dc.kv(), q, cu, dc.page_table, dc.fidelity, max(lens),
+                                              c.sm_scale, out, lse)
+        else:
+            ekv().ekv_prefill_attention(q, ws_k, ws_v, cu, dev(kv_start), max(lens), c.sm_scale, out, lse)
+        torch.cuda.synchronize()
+        outs[dtype] = (out.cpu().numpy(), lse.cpu().numpy())
+    (o32, l32), (o16, l16) = outs[torch.float32], outs[torch.float16]
+    assert f16_bits_equal_rne(o16[:T], o32[:T])
+    assert np.array_equal(l16[:T].view(np.uint32), l32[:T].view(np.uint32))
+    assert np.all(o16[T:] == 7.0) and np.all(o32[T:] == 7.0)
+    assert np.all(l16[T:] == 7.0) and np.all(l32[T:] == 7.0)
+    want, wlse = _oracle(c, pc.cu_seqlens_q, rows=np.r_[0:64, 2036:2164, T - 300:T])
+    sel = np.r_[0:64, 2036:2164, T - 300:T]
+    assert_close(o32[sel], want[sel])
+    assert_lse_close(l32[sel], wlse[sel])

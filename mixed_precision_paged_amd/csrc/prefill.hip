@@ -710,8 +710,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
 //   ds_read_b128 pass touches hit 16 distinct bank groups.  V chunk c of row
 //   r sits at chunk c ^ 4 (r % 4): the 4 rows x 64 B one transposing read
 //   pass touches hit 16 distinct bank groups.
-//   Staging: each wavefront moves 4 K and 4 V row quads (1 KiB each) per
-//   tile; lane l writes bytes 16 l of its quad, i.e. row l / 16, swizzled
+//   Staging: each of the NW wavefronts moves 16 / NW K and as many V row
+//   quads (1 KiB each) per tile; lane l writes bytes 16 l of its quad, i.e. row l / 16, swizzled
 //   chunk l % 16, so it loads the source chunk that belongs there.  Rows past
 //   the prompt are outside the descriptor range and arrive as zeros (paged
 //   source: value rows; its key rows past the prompt are masked instead).
@@ -767,7 +767,8 @@ __device__ __forceinline__ void unroll_steps(F&& f, std::integer_sequence<int, S
 // (see full_tile) with one exponential per MFMA.
 template <int NW, bool PAGED>
 __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(PrefillParams p, int n_mtiles) {
-  constexpr int RB = 1;  // 32-row blocks per wavefront (the loops below allow more)
+  constexpr int RB = 1;  // 32-row blocks per wavefront (the compute loops allow more;
+                         // the query and fp16 output staging assume one)
   constexpr int D = kWsD;
   constexpr int WR = 32 * RB;   // query rows per wavefront (RB 32-row blocks)
   constexpr int QUADS = 16 / NW;

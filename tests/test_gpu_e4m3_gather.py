@@ -118,3 +118,22 @@ def test_gather_rejects_overflow_and_marks_bad_ids():
     ok, ov = oracle.gather_compact_pages(c.k_compact, c.v_compact, c.v_scale, ids[:1], True)
     _assert_bits(gk[:1], ok)
     _assert_bits(gv[:1], ov)
+
+
+def test_scaled_gather_rounds_the_fp32_product_on_separating_scales():
+    """Every value of these pages is a case where rounding the exact product once (a fused
+    multiply-and-narrow) gives other bits than the fp32 product rounded to fp16."""
+    from rounding_cases import codes_with_significand_1_5, separating_scales
+
+    step("gather on scales that separate fp32-then-fp16 from one rounding")
+    c = synth.make_paged_case(43, [16 * 12], 32, 8, 128, compact_frac=1.0)
+    rng = np.random.default_rng(12)
+    c.v_compact[:] = codes_with_significand_1_5(c.v_compact.size, rng).reshape(c.v_compact.shape)
+    c.v_scale[:] = rng.choice(separating_scales(), size=c.v_scale.shape)
+    dc = DeviceCase(c)
+    ids = np.arange(c.v_compact.shape[0], dtype=np.int32)
+    _, gv = _gather_gpu(dc, ids, True)
+    _, ov = oracle.gather_compact_pages(c.k_compact, c.v_compact, c.v_scale, ids, True)
+    _assert_bits(gv, ov)
+    one_step = (oracle.E4M3FN_TABLE[c.v_compact] * c.v_scale.astype(np.float64)[:, None, :, None]).astype(np.float16)
+    assert np.all(gv.view(np.uint16) != one_step.view(np.uint16))

@@ -202,3 +202,21 @@ def test_long_ragged_fp16_rows_are_rne_of_fp32_and_spare_rows_untouched(route):
     sel = np.r_[0:64, 2036:2164, T - 300:T]
     assert_close(o32[sel], want[sel])
     assert_lse_close(l32[sel], wlse[sel])
+
+
+def test_direct_route_expands_separating_scales_like_the_gather():
+    """Compact pages whose every value separates the gather's fp32-then-fp16 rounding from a
+    single rounding: the direct route must still match the gather route bit for bit."""
+    from rounding_cases import codes_with_significand_1_5, separating_scales
+
+    step("paged prefill on scales that separate the two roundings")
+    lens = [300, 2100]
+    pc = synth.make_prefill_case(480, lens, 8, 2, 128)
+    c = pc.paged
+    rng = np.random.default_rng(13)
+    c.v_compact[:] = codes_with_significand_1_5(c.v_compact.size, rng).reshape(c.v_compact.shape)
+    c.v_scale[:] = rng.choice(separating_scales(), size=c.v_scale.shape) * np.float32(2.0 ** -6)
+    out, lse = _paged(c, pc.cu_seqlens_q, max(lens))
+    g_out, g_lse = _gather_route(pc)
+    assert np.array_equal(out.view(np.uint32), g_out.view(np.uint32)), "differs from the gather route"
+    assert np.array_equal(lse.view(np.uint32), g_lse.view(np.uint32))

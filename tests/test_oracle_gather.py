@@ -47,3 +47,26 @@ def test_nan_codes_become_nan():
     _, ws_v = oracle.gather_compact_pages(c.k_compact, v, c.v_scale, [0], False)
     assert np.isnan(ws_v[0, 0, 0, 0]) and np.isnan(ws_v[0, 0, 0, 1])
     assert ws_v[0, 0, 0, 2] == 0 and ws_v[0, 0, 0, 3].view(np.uint16) == 0x8000
+
+
+def test_scaled_values_round_the_fp32_product_not_the_exact_one():
+    """The scaled gather multiplies in fp32 and then rounds to fp16.  On codes 1.5 x 2^e and
+    scales where that differs from rounding the exact product once, the oracle must give
+    the two-step result for every element."""
+    from rounding_cases import codes_with_significand_1_5, separating_scales
+
+    scales = separating_scales()
+    assert scales.size == 512
+    rng = np.random.default_rng(11)
+    hkv, d = 8, 16
+    pages = 8
+    codes = codes_with_significand_1_5(pages * 16 * hkv * d, rng).reshape(pages, 16, hkv, d)
+    v_scale = rng.choice(scales, size=(pages, hkv)).astype(np.float32)
+    k = np.zeros((pages, 16, hkv, d), np.float16)
+    _, ws_v = oracle.gather_compact_pages(k, codes, v_scale, np.arange(pages, dtype=np.int32), True)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    exact = vals * v_scale.astype(np.float64)[:, None, :, None]
+    two_step = exact.astype(np.float32).astype(np.float16)
+    one_step = exact.astype(np.float16)
+    np.testing.assert_array_equal(ws_v.view(np.uint16), two_step.view(np.uint16))
+    assert np.all(ws_v.view(np.uint16) != one_step.view(np.uint16))

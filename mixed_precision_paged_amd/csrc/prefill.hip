@@ -977,18 +977,22 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[rb][i] = f32x16{};
   // Running softmax state.  Body u (below) takes the exponentials of unit
-  // u + 1 with m = m(u + 1) and finds m(u + 2) into mn; al = alpha(u + 1) =
-  // exp2(m(u) - m(u + 1)) scales l at the body's start and O after the
-  // body's P(u) products (mv: whether any row of the wavefront moved).
-  float m[RB], l[RB], al[RB], mn[RB], aln[RB];
+  // u + 1 with m = m(u + 1) and finds the scaled max of unit u + 2 into xn
+  // (mvn: whether it exceeds mtau = m + tau in any row of the wavefront).  At
+  // the body's end m(u + 2) and al = alpha(u + 2) = exp2(m(u + 1) -
+  // m(u + 2)) are formed and l is scaled by al only when some row moved
+  // (mv); O is scaled by the same factor after the next body's P.V
+  // products.  Where no row moves the factor is exactly 1, so skipping it
+  // changes no bit.
+  float m[RB], mtau[RB], l[RB], al[RB], xn[RB];
   bool mv = false, mvn = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m[rb] = kNegBig;
+    mtau[rb] = kNegBig + kTau;
     l[rb] = 0.f;
     al[rb] = 1.f;
-    mn[rb] = kNegBig;
-    aln[rb] = 1.f;
+    xn[rb] = kNegBig;
   }
 
   // Unit u = keys 32 u .. 32 u + 31 = half u % 2 of tile u / 2.
@@ -1023,35 +1027,34 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
       }
     }
   };
-  // Running max of a unit against mref, the running max before it: it moves
-  // only when the unit's max exceeds mref by more than tau.  xm: the
-  // lane's max, ym: the max of the other half-wavefront's lane (same row).
-  // Writes the new max and the factor exp2(mref - new) (exactly 1 where
-  // the max stays); returns whether any row of the wavefront moved.
-  auto new_max = [&](const float (&xm)[RB], const float (&ym)[RB], const float (&mref)[RB], float (&mout)[RB],
-                     float (&aout)[RB]) {
+  // Score maxima use the NaN-propagating maximum (v_maximum3_f32 on gfx950:
+  // no canonicalising of the MFMA results first, as fmaxf needs); masked
+  // scores are -inf, and a NaN score makes its row NaN either way.
+  auto vmax = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+  // Running max of a unit: it moves only when the unit's max exceeds the
+  // running max m by more than tau.  xm: the lane's max, ym: the max of the
+  // other half-wavefront's lane (same row).  Writes the unit's max in log2
+  // units to xn and returns whether any row of the wavefront moves.
+  auto new_max = [&](const float (&xm)[RB], const float (&ym)[RB]) {
     bool moved = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float x = fmaxf(xm[rb], ym[rb]) * p.scale_log2;
-      const float mnew = (x > mref[rb] + kTau) ? x : mref[rb];
-      moved |= mnew != mref[rb];
-      aout[rb] = fast_exp2(mref[rb] - mnew);
-      mout[rb] = mnew;
+      xn[rb] = vmax(xm[rb], ym[rb]) * p.scale_log2;
+      moved |= xn[rb] > mtau[rb];
     }
     return __ballot(moved) != 0;
   };
-  auto unit_max = [&](const f32x16 (&s)[RB], const float (&mref)[RB], float (&mout)[RB], float (&aout)[RB]) {
+  auto unit_max = [&](const f32x16 (&s)[RB]) {
     float xm[RB], ym[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float x = s[rb][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) x = fmaxf(x, s[rb][r]);
+      for (int r = 1; r < 16; ++r) x = vmax(x, s[rb][r]);
       xm[rb] = x;
       ym[rb] = shfl_xor(x, 32);
     }
-    return new_max(xm, ym, mref, mout, aout);
+    return new_max(xm, ym);
   };
   // P(u) = exp2(S(u) scale_log2 - m) as the fp16 B operands of the P.V
   // MFMAs; l sums those same fp16 values in fp32, a pair per v_dot2_f32_f16,
@@ -1094,24 +1097,28 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) asm volatile("" ::"v"(pb[rb][k2]));
   };
-  auto scale_l = [&]() {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) l[rb] *= al[rb];
-  };
   auto rescale_o = [&]() {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < DB; ++i) oacc[rb][i] *= al[rb];
   };
-  // end of a body: the next body's max and factor become current
-  auto rotate = [&](bool have_next) {
+  // End of a body: if a row's max moved, the new max and its factor become
+  // current and l is rescaled (wave-uniform branch; the empty asm keeps it
+  // a branch).
+  auto rotate = [&](bool moved) {
+    if (moved) {
+      asm volatile("");
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (have_next) m[rb] = mn[rb];
-      al[rb] = have_next ? aln[rb] : 1.f;
+      for (int rb = 0; rb < RB; ++rb) {
+        const float mnew = xn[rb] > mtau[rb] ? xn[rb] : m[rb];
+        al[rb] = fast_exp2(m[rb] - mnew);
+        m[rb] = mnew;
+        mtau[rb] = mnew + kTau;
+        l[rb] *= al[rb];
+      }
     }
-    mv = have_next && mvn;
+    mv = moved;
   };
 
   // units this wavefront computes: up to its last row's diagonal and the
@@ -1134,18 +1141,20 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   if (n_u > 0) {
     qk_unit(sB, 0);
     if (unit_needs_mask(0)) mask_unit(sB, 0);
-    unit_max(sB, m, mn, aln);  // l and O are still zero: no rescale
+    unit_max(sB);  // l and O are still zero: no rescale
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) m[rb] = mn[rb];
+    for (int rb = 0; rb < RB; ++rb) {
+      m[rb] = xn[rb] > mtau[rb] ? xn[rb] : m[rb];
+      mtau[rb] = m[rb] + kTau;
+    }
     unit_exps(sB, pA);
-    bool have1 = false;
+    bool moved1 = false;
     if (n_u > 1) {
       qk_unit(sA, 1);
       if (unit_needs_mask(1)) mask_unit(sA, 1);
-      mvn = unit_max(sA, m, mn, aln);
-      have1 = true;
+      moved1 = unit_max(sA);
     }
-    rotate(have1);
+    rotate(moved1);
   }
   __syncthreads();
 
@@ -1199,7 +1208,6 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32(a, pc[rb][k2], oacc[rb][db]);
       }
-      if constexpr (j == 0) scale_l();
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const float pv = fast_exp2(__builtin_fmaf(sc[rb][j], p.scale_log2, -m[rb]));
@@ -1217,7 +1225,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
         for (int rb = 0; rb < RB; ++rb) {
           float x = sn[rb][0];
 #pragma unroll
-          for (int r = 1; r < 8; ++r) x = fmaxf(x, sn[rb][r]);
+          for (int r = 1; r < 8; ++r) x = vmax(x, sn[rb][r]);
           xm[rb] = x;
         }
       } else if constexpr (j == 11) {
@@ -1225,12 +1233,12 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
         for (int rb = 0; rb < RB; ++rb) {
           float x = xm[rb];
 #pragma unroll
-          for (int r = 8; r < 16; ++r) x = fmaxf(x, sn[rb][r]);
+          for (int r = 8; r < 16; ++r) x = vmax(x, sn[rb][r]);
           xm[rb] = x;
           ym[rb] = shfl_xor(x, 32);
         }
       } else if constexpr (j == 14) {
-        mvn = new_max(xm, ym, m, mn, aln);
+        mvn = new_max(xm, ym);
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (j == 7) {
@@ -1241,7 +1249,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
       } else if constexpr (j == 15) {
         pin_p(pn);
         if (mv) rescale_o();
-        rotate(true);
+        rotate(mvn);
       }
     };
     unroll_steps(step, std::make_integer_sequence<int, 32>{});
@@ -1249,17 +1257,16 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   // The same for the last units of the wavefront (some parts absent).
 #define EKV_PIPE_TAIL(U, SC, SN, PC, PN)                                  \
   if ((U) < n_u) {                                                        \
-    scale_l();                                                            \
     if ((U) + 1 < n_u) unit_exps(SC, PN);                                 \
-    const bool have_next = (U) + 2 < n_u;                                 \
-    if (have_next) {                                                      \
+    bool moved_next = false;                                              \
+    if ((U) + 2 < n_u) {                                                  \
       qk_unit(SN, (U) + 2);                                               \
       if (unit_needs_mask((U) + 2)) mask_unit(SN, (U) + 2);               \
-      mvn = unit_max(SN, m, mn, aln);                                     \
+      moved_next = unit_max(SN);                                          \
     }                                                                     \
     pv_unit(PC, (U));                                                     \
     if (mv) rescale_o();                                                  \
-    rotate(have_next);                                                    \
+    rotate(moved_next);                                                   \
   }
   // Tiles whose two bodies are both complete form the main loop; every tile
   // (either loop) stages K(t + 2) and V(t + 1) and ends at the barrier.

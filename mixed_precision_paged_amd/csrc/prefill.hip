@@ -899,8 +899,13 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
     if constexpr (PAGED) {
       const int pj = 4 * t + wave / PPW;
       if (page_meta(pj) & 1) {
-        // lane l expands CPL codes of staged row l / SEGS, d CPL (l % SEGS) ..
-        constexpr int SEGS = kWave / RPW, CPL = D / SEGS;
+        // lane l expands CPL codes of staged row l / SEGS, d CPL (l % SEGS) ..,
+        // NCH 16-byte chunks of the fp16 row.  One 16-byte store pass of 16
+        // lanes holds NCH consecutive rows; the lane of row r writes its
+        // chunks starting at chunk r % NCH, so the pass covers all 16 chunk
+        // columns (the row swizzle keeps a chunk's index modulo NCH) and hits
+        // every bank group once.
+        constexpr int SEGS = kWave / RPW, CPL = D / SEGS, NCH = CPL / 8;
         const float sc = rfl(s_scale[pj]);
         const int r = lane / SEGS, sg = lane % SEGS;
         const uint8_t* cs = &vcodes[wave * RPW * D + r * D + CPL * sg];
@@ -908,11 +913,10 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
         f16* row = vbuf_of(b) + R * D;
         const int sw = 4 * (R & 3);
 #pragma unroll
-        for (int h = 0; h < CPL / 16; ++h) {
-          const uint4 c = *reinterpret_cast<const uint4*>(cs + 16 * h);
-          const int ch = (CPL / 8) * sg + 2 * h;
-          *reinterpret_cast<uint4*>(row + 8 * ((ch + 0) ^ sw)) = expand8(make_uint2(c.x, c.y), sc);
-          *reinterpret_cast<uint4*>(row + 8 * ((ch + 1) ^ sw)) = expand8(make_uint2(c.z, c.w), sc);
+        for (int j = 0; j < NCH; ++j) {
+          const int k = (j + r) & (NCH - 1);
+          const uint2 c = *reinterpret_cast<const uint2*>(cs + 8 * k);
+          *reinterpret_cast<uint4*>(row + 8 * ((NCH * sg + k) ^ sw)) = expand8(c, sc);
         }
       }
     }

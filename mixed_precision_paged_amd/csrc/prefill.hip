@@ -900,21 +900,26 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
       const int pj = 4 * t + wave / PPW;
       if (page_meta(pj) & 1) {
         // lane l expands CPL codes of staged row l / SEGS, d CPL (l % SEGS) ..,
-        // NCH 16-byte chunks of the fp16 row.  One 16-byte store pass of 16
-        // lanes holds NCH consecutive rows; the lane of row r writes its
-        // chunks starting at chunk r % NCH, so the pass covers all 16 chunk
-        // columns (the row swizzle keeps a chunk's index modulo NCH) and hits
-        // every bank group once.
+        // NCH 16-byte chunks of the fp16 row, one 8-byte code read and one
+        // 16-byte store per chunk, in the order k = j + f(r) (mod NCH), f(r)
+        // = r ^ (r >> log2 NCH): any 16 lanes (NCH consecutive rows) store to
+        // 16 distinct chunk columns (distinct k modulo NCH; the row swizzle
+        // keeps the index modulo NCH), and any 32 lanes (2 NCH rows of 128
+        // codes) read from distinct banks (distinct k in the rows 256 bytes
+        // apart), with the tile bytes and code reads of the plain order.
         constexpr int SEGS = kWave / RPW, CPL = D / SEGS, NCH = CPL / 8;
+        constexpr int LNCH = NCH == 2 ? 1 : 2;
+        static_assert(NCH == 2 || NCH == 4, "two or four chunks per lane");
         const float sc = rfl(s_scale[pj]);
         const int r = lane / SEGS, sg = lane % SEGS;
         const uint8_t* cs = &vcodes[wave * RPW * D + r * D + CPL * sg];
         const int R = RPW * wave + r;
         f16* row = vbuf_of(b) + R * D;
         const int sw = 4 * (R & 3);
+        const int fr = r ^ (r >> LNCH);
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
-          const int k = (j + r) & (NCH - 1);
+          const int k = (j + fr) & (NCH - 1);
           const uint2 c = *reinterpret_cast<const uint2*>(cs + 8 * k);
           *reinterpret_cast<uint4*>(row + 8 * ((NCH * sg + k) ^ sw)) = expand8(c, sc);
         }

@@ -172,3 +172,69 @@ def test_repeat_launches_give_identical_bits(d, hq, hkv):
             else:
                 assert torch.equal(out.view(torch.int32), first[route].view(torch.int32)), (route, rep)
     assert torch.equal(first["ws"].view(torch.int32), first["paged"].view(torch.int32))
+
+
+def _rising_scores(lens, hq, hkv, d, seed):
+    """Q, K, V (fp16) whose scores climb about 0.3 log2 units per key for the query rows whose
+    first component is +4 and fall as fast for those with -4 (alternating every three rows), on
+    top of N(0,1) noise: the running max of a climbing row moves past tau in nearly every 32-key
+    unit, that of a falling row never after its first, and every wavefront holds both kinds."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    c = (1.0 / np.sqrt(d)) * np.log2(np.e)
+    q = rng.standard_normal((T, hq, d))
+    k = rng.standard_normal((T, hkv, d))
+    v = rng.standard_normal((T, hkv, d))
+    off = 0
+    for L in lens:
+        j = np.arange(L)
+        k[off:off + L, :, 0] = (0.3 * j / (4.0 * c))[:, None]
+        q[off:off + L, :, 0] = np.where((j // 3) % 2 == 0, 4.0, -4.0)[:, None]
+        off += L
+    return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d", [([2305, 700], 32, 8, 128), ([700, 130, 33], 32, 8, 128),
+                                           ([1000, 77], 8, 2, 64)])
+def test_prefill_running_max_moving_in_most_units(lens, hq, hkv, d):
+    """Online softmax whose running max moves in most units (the rescale branch) for some rows of
+    each wavefront and never for others: both routes against the oracle, and the direct route over
+    TARGET pages bit-equal to the workspace route."""
+    step(f"prefill rising scores lens={lens} hq={hq} hkv={hkv} d={d}")
+    q, k, v = _rising_scores(lens, hq, hkv, d, 900 + d + len(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ks = cu[:-1].copy()
+    sm = 1.0 / np.sqrt(d)
+    T = q.shape[0]
+    out = torch.empty((T, hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+    ekv().ekv_prefill_attention(dev(q), dev(k), dev(v), dev(cu), dev(ks), int(max(lens)), sm, out, lse)
+    # the same rows as TARGET pages (prompt p's rows in its own pages, a permuted page order)
+    npg = [(L + 15) // 16 for L in lens]
+    pool_k = np.zeros((sum(npg), 16, hkv, d), np.float16)
+    pool_v = np.zeros_like(pool_k)
+    perm = np.random.default_rng(7).permutation(sum(npg)).astype(np.int32)
+    pt = np.zeros((len(lens), max(npg)), np.int32)
+    used = 0
+    for p, L in enumerate(lens):
+        for j in range(npg[p]):
+            r0, r1 = int(cu[p]) + 16 * j, min(int(cu[p]) + 16 * j + 16, int(cu[p + 1]))
+            pool_k[perm[used + j], :r1 - r0] = k[r0:r1]
+            pool_v[perm[used + j], :r1 - r0] = v[r0:r1]
+            pt[p, j] = perm[used + j]
+        used += npg[p]
+    kv = ekv().paged_kv(hkv, d, dev(pool_k), dev(pool_v))
+    pout = torch.empty_like(out)
+    plse = torch.empty_like(lse)
+    ekv().ekv_prefill_paged_attention(kv, dev(q), dev(cu), dev(pt), None, int(max(lens)), sm, pout, plse)
+    torch.cuda.synchronize()
+    got, glse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.array_equal(pout.cpu().numpy().view(np.uint32), got.view(np.uint32))
+    assert np.array_equal(plse.cpu().numpy().view(np.uint32), glse.view(np.uint32))
+    rng = np.random.default_rng(11)
+    sample = np.unique(np.concatenate([rng.choice(np.arange(int(cu[p]), int(cu[p + 1])),
+                                                  size=min(160, int(lens[p])), replace=False)
+                                       for p in range(len(lens))]))
+    want, wlse = oracle.prefill_attention(q, k, v, cu, ks, True, sm, rows=sample)
+    assert_close(got[sample], want[sample])
+    assert_lse_close(glse[sample], wlse[sample])

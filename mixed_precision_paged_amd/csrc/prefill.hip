@@ -752,16 +752,18 @@ __device__ __forceinline__ void unroll_steps(F&& f, std::integer_sequence<int, S
 // S(u + 1); none of the three depends on another.  The running max of a
 // unit is found in the body that produces its scores, against the running
 // max before it (deferred rescale: it moves only when the unit's max
-// exceeds it by more than tau); the factor exp2(m_old - m_new) scales l at
-// the start of the next body and O after that body's P.V products, so
-// every row sees the usual online-softmax recurrence with one rescale per
-// unit at most.  P is rounded to fp16 for the P.V MFMAs and l sums those
-// same fp16 values (v_dot2_f32_f16), so the normalisation divides by
-// exactly the weights that multiplied V.
+// exceeds it by more than tau); only when some row of the wavefront moves
+// (a wave-uniform branch) are the new max and the factor exp2(m_old -
+// m_new) formed, l scaled at the end of the body and O after the next
+// body's P.V products, so every row sees the usual online-softmax
+// recurrence with one rescale per unit at most (where no row moves the
+// factor would be exactly 1).  P is rounded to fp16 for the P.V MFMAs and
+// l sums those same fp16 values (v_dot2_f32_f16), so the normalisation
+// divides by exactly the weights that multiplied V.
 // Issue budget: one v_exp_f32 costs a wavefront about 8.5 clocks of issue
 // and a plain VALU operation about 4.7, with no overlap between the two;
 // a 32x32x16 MFMA keeps the matrix core busy 32 clocks.  A body has 16
-// MFMAs, 16 exponentials and about 60 other VALU operations per
+// MFMAs, 16 exponentials and about 48 other VALU operations per
 // wavefront, so the two wavefronts of a SIMD must interleave closely to
 // keep the matrix cores fed: the steps of a full tile are fixed in order
 // (see full_tile) with one exponential per MFMA.

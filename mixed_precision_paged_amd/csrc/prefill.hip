@@ -1258,7 +1258,11 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
         for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(l[rb]), "v"(pn[rb][0]));
         if (unit_needs_mask(2 * t + b + 2)) mask_unit(sn, 2 * t + b + 2);
       } else if constexpr (j == 15) {
+        // the body's row sums and packed weights complete ahead of the
+        // rescale branch (not sunk below it)
         pin_p(pn);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(l[rb]));
         if (mv) rescale_o();
         rotate(mvn);
       }

@@ -284,6 +284,8 @@ ekv_status ekv_gather_compact_pages(const ekv_paged_kv* kv, const int32_t* page_
  *   max_len      host bound of every len_p; > EKV_MAX_PREFILL_TOKENS returns
  *                EKV_ERR_NOT_ELIGIBLE (the caller chunks or falls back).
  *   causal       1: query i sees keys 0..i of its prompt; 0: all len_p keys.
+ *   sm_scale     softmax scale; must be finite and > 0 (EKV_ERR_INVALID_ARG
+ *                otherwise: a row's max is taken before scaling).
  *   out          [q_rows][num_q_heads][head_dim] in out_dtype (F16 = RNE of
  *                the F32 result); rows outside every prompt are not written.
  *   lse          optional fp32 [q_rows][num_q_heads], natural log.

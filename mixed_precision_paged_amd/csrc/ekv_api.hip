@@ -324,7 +324,9 @@ ekv_status ekv_prefill_attention(const void* q, int32_t q_rows, const void* k, c
     return fail(EKV_ERR_NOT_ELIGIBLE, "prompt bound %d exceeds %d tokens", max_len, EKV_MAX_PREFILL_TOKENS);
   if (causal != 0 && causal != 1) return fail(EKV_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (out_dtype != EKV_F16 && out_dtype != EKV_F32) return fail(EKV_ERR_INVALID_ARG, "out_dtype %d unknown", (int)out_dtype);
-  if (!std::isfinite(sm_scale)) return fail(EKV_ERR_INVALID_ARG, "sm_scale is not finite");
+  // the prefill kernels take a row's max before scaling and mask before scaling
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(EKV_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (n_prompts == 0 || max_len == 0) return ok();
   if (!q || !k || !v || !cu_seqlens_q || !kv_start || !out)
     return fail(EKV_ERR_INVALID_ARG, "q, k, v, cu_seqlens_q, kv_start and out are required");
@@ -369,7 +371,9 @@ ekv_status ekv_prefill_paged_attention(const ekv_paged_kv* kv, const void* q, in
     return fail(EKV_ERR_NOT_ELIGIBLE, "prompt bound %d exceeds %d tokens", max_len, EKV_MAX_PREFILL_TOKENS);
   if (causal != 0 && causal != 1) return fail(EKV_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (out_dtype != EKV_F16 && out_dtype != EKV_F32) return fail(EKV_ERR_INVALID_ARG, "out_dtype %d unknown", (int)out_dtype);
-  if (!std::isfinite(sm_scale)) return fail(EKV_ERR_INVALID_ARG, "sm_scale is not finite");
+  // the prefill kernels take a row's max before scaling and mask before scaling
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return fail(EKV_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (n_prompts == 0 || max_len == 0) return ok();
   if (!q || !cu_seqlens_q || !page_table || !out)
     return fail(EKV_ERR_INVALID_ARG, "q, cu_seqlens_q, page_table and out are required");

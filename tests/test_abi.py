@@ -149,9 +149,9 @@ def test_gather_validation():
     assert g(ctypes.byref(kv), FAKE, 0, 1, FAKE, FAKE, 4096, None) == ekv.EKV_OK
 
 
-def _prefill(max_len=8192, hq=32, hkv=8, d=128, causal=1, out=FAKE):
+def _prefill(max_len=8192, hq=32, hkv=8, d=128, causal=1, out=FAKE, sm_scale=0.088):
     return ekv._lib.ekv_prefill_attention(FAKE, 1000, FAKE, FAKE, 1000, FAKE, FAKE, 2, max_len, hq,
-                                          hkv, d, causal, 0.088, out, 0, None, None)
+                                          hkv, d, causal, sm_scale, out, 0, None, None)
 
 
 def test_prefill_validation():
@@ -160,6 +160,8 @@ def test_prefill_validation():
     assert _prefill(d=80) == ekv.EKV_ERR_UNSUPPORTED
     assert _prefill(causal=2) == ekv.EKV_ERR_INVALID_ARG
     assert _prefill(out=None) == ekv.EKV_ERR_INVALID_ARG
+    for bad in (0.0, -0.088, float("nan"), float("inf")):  # the kernels need a positive scale
+        assert _prefill(sm_scale=bad) == ekv.EKV_ERR_INVALID_ARG, bad
     assert _prefill(max_len=0) == ekv.EKV_OK
 
 
@@ -197,10 +199,10 @@ def test_quantize_validation():
     assert f(ctypes.byref(kv), FAKE, FAKE, 64, FAKE, None, FAKE, 0, None) == ekv.EKV_OK
 
 
-def _paged_prefill(kv, max_len=8192, hq=32, causal=1, out=FAKE, pt_stride=512, fidelity=FAKE):
+def _paged_prefill(kv, max_len=8192, hq=32, causal=1, out=FAKE, pt_stride=512, fidelity=FAKE, sm_scale=0.088):
     return ekv._lib.ekv_prefill_paged_attention(ctypes.byref(kv) if kv is not None else None, FAKE, 1000,
                                                 FAKE, FAKE, pt_stride, fidelity, 2, max_len, hq, causal,
-                                                0.088, out, 0, None, None)
+                                                sm_scale, out, 0, None, None)
 
 
 def test_paged_prefill_validation():
@@ -213,6 +215,8 @@ def test_paged_prefill_validation():
     assert _paged_prefill(kv, pt_stride=100) == ekv.EKV_ERR_INVALID_ARG
     assert _paged_prefill(_kv(n_t=5, n_c=5), fidelity=None) == ekv.EKV_ERR_INVALID_ARG
     assert _paged_prefill(None) == ekv.EKV_ERR_INVALID_ARG
+    for bad in (0.0, -0.088, float("nan")):
+        assert _paged_prefill(kv, sm_scale=bad) == ekv.EKV_ERR_INVALID_ARG, bad
     assert _paged_prefill(kv, max_len=0) == ekv.EKV_OK
 
 

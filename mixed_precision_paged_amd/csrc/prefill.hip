@@ -988,14 +988,14 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[rb][i] = f32x16{};
   // Running softmax state.  Body u (below) takes the exponentials of unit
-  // u + 1 with m = m(u + 1) and finds the scaled max of unit u + 2 into xn
-  // (mvn: whether it exceeds mtau = m + tau in any row of the wavefront).  At
-  // the body's end m(u + 2) and al = alpha(u + 2) = exp2(m(u + 1) -
-  // m(u + 2)) are formed and l is scaled by al only when some row moved
-  // (mv); O is scaled by the same factor after the next body's P.V
-  // products.  Where no row moves the factor is exactly 1, so skipping it
-  // changes no bit.
-  float m[RB], mtau[RB], l[RB], al[RB], xn[RB];
+  // u + 1 with m = m(u + 1) and finds the lane's max of unit u + 2 into xm
+  // (mvn: whether its scaled value exceeds mtau = m + tau in any lane of
+  // the wavefront).  At the body's end m(u + 2) and al = alpha(u + 2) =
+  // exp2(m(u + 1) - m(u + 2)) are formed and l is scaled by al only when
+  // some row moved (mv); O is scaled by the same factor after the next
+  // body's P.V products.  Where no row moves the factor is exactly 1, so
+  // skipping it changes no bit.
+  float m[RB], mtau[RB], l[RB], al[RB], xm[RB];
   bool mv = false, mvn = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -1003,7 +1003,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
     mtau[rb] = kNegBig + kTau;
     l[rb] = 0.f;
     al[rb] = 1.f;
-    xn[rb] = kNegBig;
+    xm[rb] = kNegBig;
   }
 
   // Unit u = keys 32 u .. 32 u + 31 = half u % 2 of tile u / 2.
@@ -1043,29 +1043,30 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   // scores are -inf, and a NaN score makes its row NaN either way.
   auto vmax = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
   // Running max of a unit: it moves only when the unit's max exceeds the
-  // running max m by more than tau.  xm: the lane's max, ym: the max of the
-  // other half-wavefront's lane (same row).  Writes the unit's max in log2
-  // units to xn and returns whether any row of the wavefront moves.
-  auto new_max = [&](const float (&xm)[RB], const float (&ym)[RB]) {
+  // running max m by more than tau.  A row's 32 scores of a unit lie in two
+  // lanes, l and l ^ 32, 16 each; xm holds the lane's max.  Rounding a
+  // product with the positive factor scale_log2 is monotone, so the row's
+  // scaled max exceeds mtau exactly when one of its two lanes' scaled
+  // maxima does: the wavefront-wide test needs no exchange between the
+  // halves, and the row max itself (row_max) is formed only where some row
+  // moves.  (A NaN in one half can make the test pass without a move: the
+  // row max is then NaN, m stays and the factor is exactly 1.)
+  auto moves = [&]() {
     bool moved = false;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      xn[rb] = vmax(xm[rb], ym[rb]) * p.scale_log2;
-      moved |= xn[rb] > mtau[rb];
-    }
+    for (int rb = 0; rb < RB; ++rb) moved |= xm[rb] * p.scale_log2 > mtau[rb];
     return __ballot(moved) != 0;
   };
+  auto row_max = [&](int rb) { return vmax(xm[rb], shfl_xor(xm[rb], 32)) * p.scale_log2; };
   auto unit_max = [&](const f32x16 (&s)[RB]) {
-    float xm[RB], ym[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float x = s[rb][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) x = vmax(x, s[rb][r]);
       xm[rb] = x;
-      ym[rb] = shfl_xor(x, 32);
     }
-    return new_max(xm, ym);
+    return moves();
   };
   // P(u) = exp2(S(u) scale_log2 - m) as the fp16 B operands of the P.V
   // MFMAs; l sums those same fp16 values in fp32, a pair per v_dot2_f32_f16,
@@ -1122,7 +1123,8 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
       asm volatile("");
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float mnew = xn[rb] > mtau[rb] ? xn[rb] : m[rb];
+        const float xn = row_max(rb);
+        const float mnew = xn > mtau[rb] ? xn : m[rb];
         al[rb] = fast_exp2(m[rb] - mnew);
         m[rb] = mnew;
         mtau[rb] = mnew + kTau;
@@ -1155,7 +1157,8 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
     unit_max(sB);  // l and O are still zero: no rescale
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      m[rb] = xn[rb] > mtau[rb] ? xn[rb] : m[rb];
+      const float xn = row_max(rb);
+      m[rb] = xn > mtau[rb] ? xn : m[rb];
       mtau[rb] = m[rb] + kTau;
     }
     unit_exps(sB, pA);
@@ -1178,8 +1181,8 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   // the LDS read of the operand of step j + kAhead, the exponential of
   // score j of S(u + 1) (l scaled first at j 0, fp16 pairs packed at odd
   // j), and from j 10 on the running max of S(u + 2): the lane max (j 10,
-  // 11; the cross-half exchange goes through LDS) and the new max and
-  // factor (j 14).  One transcendental and a few plain VALU operations per
+  // 11) and the wavefront's move test (j 14); the row max and the factor
+  // follow at the body's end, only where some row moves.  One transcendental and a few plain VALU operations per
   // MFMA keep the vector ALUs under the matrix cores' time.  Only the first
   // kAhead reads after the tile's barrier can stall the matrix cores.
   constexpr int kAhead = 3;
@@ -1201,7 +1204,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
     f16x8 ring[kAhead + 1];
 #pragma unroll
     for (int s = 0; s < kAhead; ++s) ring[s] = operand(s);
-    float xm[RB], ym[RB], pe[RB];
+    float pe[RB];
     auto step = [&](auto step_index) {
       constexpr int s = decltype(step_index)::value;
       constexpr int b = s >> 4, j = s & 15;
@@ -1246,10 +1249,9 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
 #pragma unroll
           for (int r = 8; r < 16; ++r) x = vmax(x, sn[rb][r]);
           xm[rb] = x;
-          ym[rb] = shfl_xor(x, 32);
         }
       } else if constexpr (j == 14) {
-        mvn = new_max(xm, ym);
+        mvn = moves();
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (j == 7) {

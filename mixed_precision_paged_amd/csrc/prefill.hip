@@ -59,6 +59,7 @@ constexpr int kM = 128;        // query rows per workgroup
 constexpr int kN = 64;         // keys per tile
 constexpr int kThreads = 256;
 constexpr float kTau = 8.0f;
+constexpr float kOver = 256.0f;  // 2^kTau: a lane's weight sum of one unit that starts a rescale
 constexpr float kNegBig = -1.0e30f;
 constexpr int kXcds = 8;
 constexpr int kMaxPromptPages = 512;  // paged source: prompts of at most 8192 tokens
@@ -749,21 +750,21 @@ __device__ __forceinline__ void unroll_steps(F&& f, std::integer_sequence<int, S
 // The loop runs over 32-key units u (half a 64-key tile) as a three-stage
 // software pipeline: body u computes S(u + 2) = K Q^T and O += V(u)^T P(u)
 // on the matrix cores while the vector ALUs take the exponentials of
-// S(u + 1); none of the three depends on another.  The running max of a
-// unit is found in the body that produces its scores, against the running
-// max before it (deferred rescale: it moves only when the unit's max
-// exceeds it by more than tau); only when some row of the wavefront moves
-// (a wave-uniform branch) are the new max and the factor exp2(m_old -
-// m_new) formed, l scaled at the end of the body and O after the next
-// body's P.V products, so every row sees the usual online-softmax
-// recurrence with one rescale per unit at most (where no row moves the
-// factor would be exactly 1).  P is rounded to fp16 for the P.V MFMAs and
-// l sums those same fp16 values (v_dot2_f32_f16), so the normalisation
-// divides by exactly the weights that multiplied V.
+// S(u + 1); none of the three depends on another.  A unit's exponentials
+// are taken against the running max as it stands (deferred rescale): each
+// lane sums its 16 weights of the unit, and only where some lane's sum
+// exceeds 2^tau (a wave-uniform branch, rare once the max has settled)
+// do the rows concerned take the unit's max, scale l and O by exp2(m_old -
+// m_new) and take the unit's exponentials again.  Every weight is thus at
+// most 2^tau, and each row sees the usual online-softmax recurrence with
+// at most one rescale per unit (a row that keeps its max gets the factor
+// 1 and the same weights, bit for bit).  P is rounded to fp16 for the P.V
+// MFMAs and l sums those same fp16 values (v_dot2_f32_f16), so the
+// normalisation divides by exactly the weights that multiplied V.
 // Issue budget: one v_exp_f32 costs a wavefront about 8.5 clocks of issue
 // and a plain VALU operation about 4.7, with no overlap between the two;
 // a 32x32x16 MFMA keeps the matrix core busy 32 clocks.  A body has 16
-// MFMAs, 16 exponentials and about 48 other VALU operations per
+// MFMAs, 16 exponentials and about 40 other VALU operations per
 // wavefront, so the two wavefronts of a SIMD must interleave closely to
 // keep the matrix cores fed: the steps of a full tile are fixed in order
 // (see full_tile) with one exponential per MFMA.
@@ -987,23 +988,16 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[rb][i] = f32x16{};
-  // Running softmax state.  Body u (below) takes the exponentials of unit
-  // u + 1 with m = m(u + 1) and finds the lane's max of unit u + 2 into xm
-  // (mvn: whether its scaled value exceeds mtau = m + tau in any lane of
-  // the wavefront).  At the body's end m(u + 2) and al = alpha(u + 2) =
-  // exp2(m(u + 1) - m(u + 2)) are formed and l is scaled by al only when
-  // some row moved (mv); O is scaled by the same factor after the next
-  // body's P.V products.  Where no row moves the factor is exactly 1, so
-  // skipping it changes no bit.
-  float m[RB], mtau[RB], l[RB], al[RB], xm[RB];
-  bool mv = false, mvn = false;
+  // Running softmax state: max m (log2 units), row sum l (this lane's
+  // half of the row's keys) and ls, the lane's sum of the weights of the
+  // unit whose exponentials are being taken.  O and l always hold the
+  // units before it against the current m.
+  float m[RB], l[RB], ls[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m[rb] = kNegBig;
-    mtau[rb] = kNegBig + kTau;
     l[rb] = 0.f;
-    al[rb] = 1.f;
-    xm[rb] = kNegBig;
+    ls[rb] = 0.f;
   }
 
   // Unit u = keys 32 u .. 32 u + 31 = half u % 2 of tile u / 2.
@@ -1042,35 +1036,18 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   // no canonicalising of the MFMA results first, as fmaxf needs); masked
   // scores are -inf, and a NaN score makes its row NaN either way.
   auto vmax = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
-  // Running max of a unit: it moves only when the unit's max exceeds the
-  // running max m by more than tau.  A row's 32 scores of a unit lie in two
-  // lanes, l and l ^ 32, 16 each; xm holds the lane's max.  Rounding a
-  // product with the positive factor scale_log2 is monotone, so the row's
-  // scaled max exceeds mtau exactly when one of its two lanes' scaled
-  // maxima does: the wavefront-wide test needs no exchange between the
-  // halves, and the row max itself (row_max) is formed only where some row
-  // moves.  (A NaN in one half can make the test pass without a move: the
-  // row max is then NaN, m stays and the factor is exactly 1.)
-  auto moves = [&]() {
-    bool moved = false;
+  // The row max of a unit's scores in log2 units: a row's 32 scores lie in
+  // two lanes, l and l ^ 32, 16 each (scale_log2 > 0 keeps the max).
+  auto row_max = [&](const f32x16& s) {
+    float x = s[0];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) moved |= xm[rb] * p.scale_log2 > mtau[rb];
-    return __ballot(moved) != 0;
-  };
-  auto row_max = [&](int rb) { return vmax(xm[rb], shfl_xor(xm[rb], 32)) * p.scale_log2; };
-  auto unit_max = [&](const f32x16 (&s)[RB]) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float x = s[rb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) x = vmax(x, s[rb][r]);
-      xm[rb] = x;
-    }
-    return moves();
+    for (int r = 1; r < 16; ++r) x = vmax(x, s[r]);
+    return vmax(x, shfl_xor(x, 32)) * p.scale_log2;
   };
   // P(u) = exp2(S(u) scale_log2 - m) as the fp16 B operands of the P.V
-  // MFMAs; l sums those same fp16 values in fp32, a pair per v_dot2_f32_f16,
-  // so the normalisation divides by exactly the weights that multiplied V.
+  // MFMAs; ls sums those same fp16 values in fp32, a pair per
+  // v_dot2_f32_f16, so the normalisation divides by exactly the weights
+  // that multiplied V.
   auto unit_exps = [&](const f32x16 (&s)[RB], f16x8 (&pn)[RB][2]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -1079,7 +1056,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
         const float p0 = fast_exp2(__builtin_fmaf(s[rb][e], p.scale_log2, -m[rb]));
         const float p1 = fast_exp2(__builtin_fmaf(s[rb][e + 1], p.scale_log2, -m[rb]));
         const f16x2 pr = {(f16)p0, (f16)p1};
-        l[rb] = __builtin_amdgcn_fdot2(pr, f16x2{(f16)1.0f, (f16)1.0f}, l[rb], false);
+        ls[rb] = __builtin_amdgcn_fdot2(pr, f16x2{(f16)1.0f, (f16)1.0f}, e == 0 ? 0.f : ls[rb], false);
         pn[rb][e / 8][e % 8] = pr[0];
         pn[rb][e / 8][e % 8 + 1] = pr[1];
       }
@@ -1109,29 +1086,33 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) asm volatile("" ::"v"(pb[rb][k2]));
   };
-  auto rescale_o = [&]() {
+  // Ends the softmax of unit u + 1 once O holds P(u): a lane whose weights
+  // of the unit sum past 2^tau (NaN sums do not) sends its row to the
+  // unit's max; l and O are scaled by exp2(m_old - m_new) and the unit's
+  // exponentials taken again (wave-uniform branch; the empty asm keeps it
+  // a branch).  Rows that keep their max get the factor 1 and the same
+  // weights.  Then l takes the unit's sum.
+  auto settle = [&](const f32x16 (&s)[RB], f16x8 (&pn)[RB][2]) {
+    bool over = false;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int i = 0; i < DB; ++i) oacc[rb][i] *= al[rb];
-  };
-  // End of a body: if a row's max moved, the new max and its factor become
-  // current and l is rescaled (wave-uniform branch; the empty asm keeps it
-  // a branch).
-  auto rotate = [&](bool moved) {
-    if (moved) {
+    for (int rb = 0; rb < RB; ++rb) over |= ls[rb] > kOver;
+    if (__ballot(over) != 0) {
       asm volatile("");
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float xn = row_max(rb);
-        const float mnew = xn > mtau[rb] ? xn : m[rb];
-        al[rb] = fast_exp2(m[rb] - mnew);
+        const float lsp = shfl_xor(ls[rb], 32), xn = row_max(s[rb]);  // whole wavefront
+        const bool row_over = (ls[rb] > kOver) | (lsp > kOver);
+        const float mnew = row_over ? vmax(m[rb], xn) : m[rb];
+        const float al = fast_exp2(m[rb] - mnew);
         m[rb] = mnew;
-        mtau[rb] = mnew + kTau;
-        l[rb] *= al[rb];
+        l[rb] *= al;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) oacc[rb][i] *= al;
       }
+      unit_exps(s, pn);
     }
-    mv = moved;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l[rb] += ls[rb];
   };
 
   // units this wavefront computes: up to its last row's diagonal and the
@@ -1154,21 +1135,15 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   if (n_u > 0) {
     qk_unit(sB, 0);
     if (unit_needs_mask(0)) mask_unit(sB, 0);
-    unit_max(sB);  // l and O are still zero: no rescale
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float xn = row_max(rb);
-      m[rb] = xn > mtau[rb] ? xn : m[rb];
-      mtau[rb] = m[rb] + kTau;
-    }
+    for (int rb = 0; rb < RB; ++rb) m[rb] = vmax(row_max(sB[rb]), kNegBig);  // l and O are zero
     unit_exps(sB, pA);
-    bool moved1 = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l[rb] = ls[rb];
     if (n_u > 1) {
       qk_unit(sA, 1);
       if (unit_needs_mask(1)) mask_unit(sA, 1);
-      moved1 = unit_max(sA);
     }
-    rotate(moved1);
   }
   __syncthreads();
 
@@ -1178,11 +1153,9 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   //   j < 8:  the MFMA(s) of k-step j of S(u + 2)             (operand: K)
   //   j >= 8: the MFMA(s) of O += V(u)^T P(u) for (k2, db) =
   //           ((j - 8) / 4, (j - 8) % 4)                      (operand: V^T)
-  // the LDS read of the operand of step j + kAhead, the exponential of
-  // score j of S(u + 1) (l scaled first at j 0, fp16 pairs packed at odd
-  // j), and from j 10 on the running max of S(u + 2): the lane max (j 10,
-  // 11) and the wavefront's move test (j 14); the row max and the factor
-  // follow at the body's end, only where some row moves.  One transcendental and a few plain VALU operations per
+  // the LDS read of the operand of step j + kAhead and the exponential of
+  // score j of S(u + 1) (fp16 pairs packed and summed at odd j); the
+  // unit's softmax is settled at the body's end.  One transcendental and a few plain VALU operations per
   // MFMA keep the vector ALUs under the matrix cores' time.  Only the first
   // kAhead reads after the tile's barrier can stall the matrix cores.
   constexpr int kAhead = 3;
@@ -1229,44 +1202,20 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
           pe[rb] = pv;
         } else {
           const f16x2 pr = {(f16)pe[rb], (f16)pv};
-          l[rb] = __builtin_amdgcn_fdot2(pr, f16x2{(f16)1.0f, (f16)1.0f}, l[rb], false);
+          ls[rb] = __builtin_amdgcn_fdot2(pr, f16x2{(f16)1.0f, (f16)1.0f}, j == 1 ? 0.f : ls[rb], false);
           pn[rb][j / 8][(j % 8) - 1] = pr[0];
           pn[rb][j / 8][j % 8] = pr[1];
         }
-      }
-      if constexpr (j == 10) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          float x = sn[rb][0];
-#pragma unroll
-          for (int r = 1; r < 8; ++r) x = vmax(x, sn[rb][r]);
-          xm[rb] = x;
-        }
-      } else if constexpr (j == 11) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          float x = xm[rb];
-#pragma unroll
-          for (int r = 8; r < 16; ++r) x = vmax(x, sn[rb][r]);
-          xm[rb] = x;
-        }
-      } else if constexpr (j == 14) {
-        mvn = moves();
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (j == 7) {
         // the first eight exponentials stay ahead of the mask branch
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(l[rb]), "v"(pn[rb][0]));
+        for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(ls[rb]), "v"(pn[rb][0]));
         if (unit_needs_mask(2 * t + b + 2)) mask_unit(sn, 2 * t + b + 2);
       } else if constexpr (j == 15) {
-        // the body's row sums and packed weights complete ahead of the
-        // rescale branch (not sunk below it)
         pin_p(pn);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(l[rb]));
-        if (mv) rescale_o();
-        rotate(mvn);
+        settle(sc, pn);
       }
     };
     unroll_steps(step, std::make_integer_sequence<int, 32>{});
@@ -1275,15 +1224,12 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
 #define EKV_PIPE_TAIL(U, SC, SN, PC, PN)                                  \
   if ((U) < n_u) {                                                        \
     if ((U) + 1 < n_u) unit_exps(SC, PN);                                 \
-    bool moved_next = false;                                              \
     if ((U) + 2 < n_u) {                                                  \
       qk_unit(SN, (U) + 2);                                               \
       if (unit_needs_mask((U) + 2)) mask_unit(SN, (U) + 2);               \
-      moved_next = unit_max(SN);                                          \
     }                                                                     \
     pv_unit(PC, (U));                                                     \
-    if (mv) rescale_o();                                                  \
-    rotate(moved_next);                                                   \
+    if ((U) + 1 < n_u) settle(SC, PN);                                    \
   }
   // Tiles whose two bodies are both complete form the main loop; every tile
   // (either loop) stages K(t + 2) and V(t + 1) and ends at the barrier.

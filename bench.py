@@ -504,7 +504,8 @@ def bench_prefill(args):
                                "head dim 128, causal, 4,096-page workspace, 4 chunks of 8 prompts (seed 4)"},
         "roofline": {"bound": "mfma", "kernel": "ekv_prefill_attention (prefill_pipe_kernel)",
                      "achieved": round(tflops, 1), "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_FP16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / MFMA_FP16_PEAK_TFLOPS, 4),
+                     "traffic": counted_prefill_traffic(),
                      "avg_call_us": round(p * 1e6, 1), "flops_per_call": flops},
         "prefill": {"avg_chunk_ms": round(p * 1e3, 3), "flops_per_chunk": flops,
                     "tflops": round(tflops, 1), "peak_tflops": MFMA_FP16_PEAK_TFLOPS,
@@ -838,31 +839,51 @@ def bench_elastic(args):
 
 # ----------------------------------------------------------------- counters
 
-def counted_traffic(pps):
-    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, or None when the decode kernel code or the split plan changed since it
-    was taken."""
+def pmc_record(name):
+    """The JSON record of a committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None."""
     import re
 
-    path = os.path.join(ROOT, "profiles", "decode_compact_b32_ctx8192_pmc.md")
     try:
-        text = open(path).read()
-        rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
-        h = decode_code_hash()
+        text = open(os.path.join(ROOT, "profiles", name)).read()
+        return json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
     except (OSError, AttributeError, ValueError):
         return None
-    same = rec.get("kernel_code_sha256") == h and rec.get("pages_per_split") == pps
+
+
+def counted_traffic(pps):
+    """HBM bytes per decode call from the committed counter summary, or None when the
+    decode kernel code or the split plan changed since it was taken."""
+    rec = pmc_record("decode_compact_b32_ctx8192_pmc.md")
+    if rec is None:
+        return None
+    same = rec.get("kernel_code_sha256") == decode_code_hash() and rec.get("pages_per_split") == pps
     return int(rec["traffic_bytes_per_call"]) if same else None
 
 
+def counted_prefill_traffic():
+    """HBM bytes per workspace prefill call (8 x 8192 chunk) from the committed counter
+    summary, or None when the prefill kernel code changed since it was taken."""
+    rec = pmc_record("prefill_route_32x8192_pmc.md")
+    if rec is None or rec.get("kernel_code_sha256") != prefill_code_hash():
+        return None
+    return int(rec["traffic_bytes_per_call"])
+
+
 def decode_code_hash():
-    """sha256 of the decode kernel's sources with comments and whitespace removed: it
-    changes when the compiled code can, not when a comment does."""
+    return code_hash(("decode.hip", "ekv_device.hpp", "ekv_internal.hpp"))
+
+
+def prefill_code_hash():
+    return code_hash(("prefill.hip", "ekv_device.hpp", "ekv_internal.hpp"))
+
+
+def code_hash(files):
+    """sha256 of a kernel's sources with comments and whitespace removed: it changes
+    when the compiled code can, not when a comment does."""
     import hashlib
     import re
 
-    srcs = [os.path.join(ROOT, "mixed_precision_paged_amd", "csrc", f)
-            for f in ("decode.hip", "ekv_device.hpp", "ekv_internal.hpp")]
+    srcs = [os.path.join(ROOT, "mixed_precision_paged_amd", "csrc", f) for f in files]
     code = []
     for f in srcs:
         t = open(f).read()

@@ -395,3 +395,40 @@ def test_bench_cpu_baseline_pool_runs_the_oracle():
     assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
     assert 1 <= r["cores"] <= bench.CPU_WORKERS_MAX
     assert "4 (sequence, KV head) tasks" in r["sample"]
+
+
+def test_bench_counted_traffic_follows_the_kernel_source(monkeypatch):
+    """bench.py reports a kernel's counted HBM traffic only while the committed counter
+    record's source hash matches the kernel's sources (comments and spacing aside)."""
+    import sys
+
+    sys.path.insert(0, ROOT)
+    import bench
+
+    rec = bench.pmc_record("prefill_route_32x8192_pmc.md")
+    assert rec["traffic_bytes_per_call"] >= rec["algorithmic_bytes_per_call"] > 0
+    h = bench.prefill_code_hash()
+    monkeypatch.setattr(bench, "prefill_code_hash", lambda: h)
+    want = int(rec["traffic_bytes_per_call"]) if rec["kernel_code_sha256"] == h else None
+    assert bench.counted_prefill_traffic() == want
+    monkeypatch.setattr(bench, "prefill_code_hash", lambda: "0" * 64)
+    assert bench.counted_prefill_traffic() is None
+    # a comment or a change of spacing leaves the hash alone; code does not
+    src = os.path.join(ROOT, "mixed_precision_paged_amd", "csrc", "prefill.hip")
+    text = open(src).read()
+    real_open = open
+
+    def fake_open(path, *a, **k):
+        if os.path.abspath(str(path)) == os.path.abspath(src):
+            import io
+            return io.StringIO(fake_open.text)
+        return real_open(path, *a, **k)
+
+    monkeypatch.setattr("builtins.open", fake_open)
+    fake_open.text = "// a new comment\n" + text.replace("\n", "\n  ", 3)
+    with_comment = bench.code_hash(("prefill.hip",))
+    fake_open.text = text
+    plain = bench.code_hash(("prefill.hip",))
+    assert with_comment == plain
+    fake_open.text = text + "\nint extra_symbol;\n"
+    assert bench.code_hash(("prefill.hip",)) != plain

@@ -317,9 +317,13 @@ ekv_status ekv_prefill_attention(const void* q, int32_t q_rows, const void* k, c
  *   causal, sm_scale, out, out_dtype, lse: as in ekv_prefill_attention.
  * Values: a TARGET page's FP16 V as stored; a compact page's V as
  * fp16(fp32(e4m3) * fp32(scale)) — the scaled gather's values, so the result
- * equals gather + ekv_prefill_attention bit for bit.  A 128-row tile of a
- * prompt whose keys include an out-of-pool page id or an unknown flag is
- * written as NaN; an over-long prompt (len > max_len) is written as NaN.
+ * equals gather + ekv_prefill_attention bit for bit.  A page with an
+ * out-of-pool id or an unknown flag poisons its prompt from the start of
+ * the 64-token key tile that holds it: those rows (every causal row that
+ * attends to the page among them) are written as NaN, and so may be up to
+ * 255 rows before it (the rows sharing a workgroup with them); earlier
+ * rows are computed.  Without the causal mask the whole prompt is NaN.  An
+ * over-long prompt (len > max_len) is written as NaN.
  */
 ekv_status ekv_prefill_paged_attention(const ekv_paged_kv* kv, const void* q, int32_t q_rows,
                                        const int32_t* cu_seqlens_q, const int32_t* page_table,

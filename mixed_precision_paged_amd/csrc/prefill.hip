@@ -357,6 +357,35 @@ __device__ void write_nan_rows(const PrefillParams& p, int64_t q0, int r_lo, int
 struct WorkItem {
   int prompt, h, mt;
 };
+// Heads per workgroup of the head-dim-128 kernel.  At 4 wavefronts: the
+// largest power of two dividing both the GQA group size G and 4, so that
+// the wavefronts take HW query heads of one KV head times 4 / HW blocks of
+// 32 positions and every wavefront of a causal workgroup ends within one
+// 32-key unit of the others (one head per workgroup spreads them over 4
+// units, and the early ones idle while the last ones finish): 3.0-3.6%
+// faster on 512-1,500-token prompts.  At 8 wavefronts one head of 256
+// positions measured as fast or faster on prompts of whole 256-row tiles
+// (4 x 2048 1.9%, the paged source 1-3%), so those keep it.
+__host__ __device__ __forceinline__ int heads_per_workgroup(int G, int NW) {
+  if (NW != 4) return 1;
+  const int low = G & -G;
+  return low < NW ? low : NW;
+}
+// (prompt, first query head, row tile) of a workgroup of HW heads; the
+// order is that of work_item, over groups of HW heads instead of heads.
+__device__ __forceinline__ WorkItem work_item_heads(const PrefillParams& p, int n_mtiles, int HW) {
+  const int total = (int)gridDim.x;
+  const int bid = blockIdx.x;
+  const int work = (total % kXcds == 0) ? (bid % kXcds) * (total / kXcds) + bid / kXcds : bid;
+  const int GW = p.num_q_heads / p.num_kv_heads / HW;  // head groups per KV head
+  const int per_group = GW * n_mtiles;
+  const int grp = work / per_group, r = work % per_group;
+  WorkItem wi;
+  wi.mt = n_mtiles - 1 - r / GW;
+  wi.h = ((grp % p.num_kv_heads) * GW + r % GW) * HW;
+  wi.prompt = grp / p.num_kv_heads;
+  return wi;
+}
 __device__ __forceinline__ WorkItem work_item(const PrefillParams& p, int n_mtiles) {
   const int total = (int)gridDim.x;
   const int bid = blockIdx.x;
@@ -802,22 +831,25 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   constexpr bool QST = NW == 8;
   __shared__ __attribute__((aligned(1024))) f16 qst[QST ? NW * 32 * kWsD : 8];
 
-  const WorkItem wi = work_item(p, n_mtiles);
-  const int prompt = wi.prompt, h = wi.h, mt = wi.mt;
   const int G = p.num_q_heads / p.num_kv_heads;
-  const int g = h / G;
+  const int HW = heads_per_workgroup(G, NW);  // query heads of this workgroup
+  const int WB = WR * (NW / HW);              // positions of this workgroup
+  const WorkItem wi = work_item_heads(p, n_mtiles, HW);
+  const int prompt = wi.prompt, h0 = wi.h, mt = wi.mt;
+  const int g = h0 / G;
 
   const int q0 = p.cu_seqlens_q[prompt];
   const int q1 = p.cu_seqlens_q[prompt + 1];
   if (q0 < 0 || q1 < q0 || q1 > p.q_rows) return;  // rows not addressable: nothing to write
   const int L = q1 - q0;
-  const int m0 = mt * WR * NW;
+  const int m0 = mt * WB;
   const int kv0 = PAGED ? 0 : p.kv_start[prompt];
   const bool ok = PAGED ? (L <= p.max_len && L <= kMaxPromptPages * kPage &&
                            (int64_t)L <= (int64_t)p.pt_stride * kPage)
                         : (L <= p.max_len && kv0 >= 0 && (int64_t)kv0 + L <= p.kv_rows);
   if (!ok) {
-    if (mt == 0) write_nan_rows<D>(p, q0, 0, L, h);
+    if (mt == 0)
+      for (int hh = 0; hh < HW; ++hh) write_nan_rows<D>(p, q0, 0, L, h0 + hh);
     return;
   }
   if (m0 >= L) return;
@@ -825,16 +857,18 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int r0 = m0 + WR * wave;
+  // wavefront w: head h0 + w % HW, block w / HW of 32 positions
+  const int h = h0 + wave % HW;
+  const int r0 = m0 + WR * (wave / HW);
   const int64_t hq_row = (int64_t)p.num_q_heads * D;
-  const int n_end = p.causal ? min(L, m0 + WR * NW) : L;
+  const int n_end = p.causal ? min(L, m0 + WB) : L;
   const int n_tiles = (n_end + kN - 1) / kN;
   const uint32_t rowb = (uint32_t)p.num_kv_heads * D * 2u;
   const uint32_t rowb8 = (uint32_t)p.num_kv_heads * D;
 
   if constexpr (PAGED) {
     if (!stage_page_meta(p, prompt, g, L, 4 * n_tiles, s_meta, s_scale, &s_bad)) {
-      write_nan_rows<D>(p, q0, m0, min(L, m0 + WR * NW), h);
+      for (int hh = 0; hh < HW; ++hh) write_nan_rows<D>(p, q0, m0, min(L, m0 + WB), h0 + hh);
       return;
     }
   }
@@ -1337,8 +1371,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (paged && p.max_len > kMaxPromptPages * kPage) return hipErrorInvalidValue;
   if (p.head_dim == kWsD) {
     const int nw = p.max_len >= kLongPrompt ? 8 : 4;
-    const int n_mt = (p.max_len + 32 * nw - 1) / (32 * nw);
-    const dim3 g((unsigned)((int64_t)n_mt * p.num_q_heads * p.n_prompts)), blk(nw * kWave);
+    const int hw = heads_per_workgroup(p.num_q_heads / p.num_kv_heads, nw);
+    const int wb = 32 * (nw / hw);
+    const int n_mt = (p.max_len + wb - 1) / wb;
+    const dim3 g((unsigned)((int64_t)n_mt * (p.num_q_heads / hw) * p.n_prompts)), blk(nw * kWave);
     if (paged && nw == 8) hipLaunchKernelGGL((prefill_pipe_kernel<8, true>), g, blk, 0, stream, p, n_mt);
     else if (paged) hipLaunchKernelGGL((prefill_pipe_kernel<4, true>), g, blk, 0, stream, p, n_mt);
     else if (nw == 8) hipLaunchKernelGGL((prefill_pipe_kernel<8, false>), g, blk, 0, stream, p, n_mt);

@@ -106,6 +106,9 @@ def test_fp16_output_and_single_pool_without_flags():
 
 
 def test_bad_page_id_marks_its_row_tiles_nan():
+    """An out-of-pool page id poisons the rows of every workgroup that stages its key tile.
+    Below 2,048 tokens, with 4 query heads per KV head, a workgroup holds 32 positions of 4
+    heads, so exactly the rows from the start of the bad page's 64-key tile are NaN."""
     step("paged prefill bad page id")
     lens = [400, 60]
     pc = synth.make_prefill_case(430, lens, 8, 2, 128)
@@ -150,12 +153,15 @@ def test_long_ragged_mixed_fidelity_prompts_match_oracle(causal):
 
 
 def test_bad_page_id_in_a_long_prompt_marks_its_256_row_tiles_nan():
+    """From 2,048 tokens a workgroup holds 256 positions of one head: rows 640.. read the bad
+    page's tile, so the workgroup of rows 512..767 and every later one is NaN; every earlier
+    row is computed and matches the oracle."""
     step("paged prefill bad page id, 256-row workgroups")
     lens = [2100, 60]
     pc = synth.make_prefill_case(460, lens, 8, 2, 128)
     c = pc.paged
     pt = c.page_table.copy()
-    pt[0, 40] = c.k_compact.shape[0] + 5          # keys 640..655 of prompt 0: row tiles 2.. read it
+    pt[0, 40] = c.k_compact.shape[0] + 5          # keys 640..655 of prompt 0: rows 640.. read it
     out, lse = _paged(c, pc.cu_seqlens_q, max(lens), pt=pt)
     assert np.all(np.isnan(out[512:2100])) and np.all(np.isnan(lse[512:2100]))
     assert np.all(np.isfinite(out[:512])) and np.all(np.isfinite(out[2100:]))

@@ -47,8 +47,11 @@ def _oracle_route(pc, prompts, rows, cu, kv_start, apply_scale=True, causal=True
     return oracle.prefill_attention(c.q[rows], wk, wv, cu, kv_start, causal, c.sm_scale, rows=sample)
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (8, 2, 128), (16, 2, 64), (16, 8, 128), (4, 2, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (8, 2, 128), (16, 2, 64), (16, 8, 128), (4, 2, 64),
+                                      (16, 2, 128)])
 def test_prefill_route_ragged_prompts(hq, hkv, d):
+    """Ragged prompts, every GQA group size: below 2,048 tokens a head-dim-128 workgroup
+    takes 1, 2 or 4 query heads of one KV head (8 per KV head: two such groups)."""
     step(f"prefill ragged hq={hq} hkv={hkv} d={d}")
     lens = [1, 17, 100, 257, 64, 130]
     pc = synth.make_prefill_case(200 + d + hq, lens, hq, hkv, d)

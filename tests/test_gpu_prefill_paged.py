@@ -49,7 +49,8 @@ def _gather_route(pc):
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 2, 64), (8, 8, 128), (16, 2, 64), (16, 8, 128), (4, 2, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 2, 64), (8, 8, 128), (16, 2, 64), (16, 8, 128), (4, 2, 64),
+                                      (32, 4, 128)])
 def test_compact_prompts_bit_equal_to_gather_route_and_match_oracle(hq, hkv, d):
     step(f"paged prefill compact hq={hq} hkv={hkv} d={d}")
     lens = [1, 17, 100, 257, 64, 130]

@@ -1196,8 +1196,9 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   // The tile parity (which of the two K and V buffers) is a compile-time
   // constant, so every LDS operand address is a fixed register plus an
   // immediate offset.
-  auto full_tile = [&](int t, auto parity) {
+  auto full_tile = [&](int t, auto parity, auto masked) {
     constexpr int par = decltype(parity)::value;
+    constexpr bool MASKED = decltype(masked)::value;
     const f16* kt = (par ^ 1) ? kb1 : kb0;  // K(t + 1): S(2t + 2) (keys 0..31), S(2t + 3)
     const f16* vt = par ? vb1 : vb0;        // V(t): P(2t) (kk 0, 1), P(2t + 1) (kk 2, 3)
     auto operand = [&](int s) -> f16x8 {
@@ -1246,7 +1247,8 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
         // the first eight exponentials stay ahead of the mask branch
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(ls[rb]), "v"(pn[rb][0]));
-        if (unit_needs_mask(2 * t + b + 2)) mask_unit(sn, 2 * t + b + 2);
+        if constexpr (MASKED)
+          if (unit_needs_mask(2 * t + b + 2)) mask_unit(sn, 2 * t + b + 2);
       } else if constexpr (j == 15) {
         pin_p(pn);
         settle(sc, pn);
@@ -1269,21 +1271,36 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void prefill_pipe_kernel(Prefil
   // (either loop) stages K(t + 2) and V(t + 1) and ends at the barrier.
   const int n_full = max(0, min(n_tiles, (n_u - 2) / 2));
   int it = 0;
-  auto main_tile = [&](int t, auto parity) {
+  auto main_tile = [&](int t, auto parity, auto masked) {
     constexpr int par = decltype(parity)::value;
     if (t + 2 < n_tiles) stage_k(t + 2, par);
     if (t + 1 < n_tiles) stage_v(t + 1, par ^ 1);
-    full_tile(t, parity);
+    full_tile(t, parity, masked);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     if (t + 1 < n_tiles) put_v(t + 1, par ^ 1);
     __syncthreads();
   };
+  // Whether a unit needs its mask only grows with the unit (the diagonal,
+  // then the prompt's end), so at 8 wavefronts the full tiles before the
+  // first such unit run a copy of the tile without the mask test and its
+  // branch (1-3% on long prompts; at 4 wavefronts the second copy costs
+  // registers and is slower).
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if constexpr (NW == 8) {
+    const int first_masked = min(p.causal ? r0 / 32 : L / 32, L / 32);
+    const int n_clean = min(n_full, max(0, (first_masked - 2) / 2));  // full tiles t with 2 t + 3 < first_masked
+    for (; it + 1 < n_clean; it += 2) {
+      main_tile(it, I0{}, std::false_type{});
+      main_tile(it + 1, I1{}, std::false_type{});
+    }
+  }
   for (; it + 1 < n_full; it += 2) {
-    main_tile(it, std::integral_constant<int, 0>{});
-    main_tile(it + 1, std::integral_constant<int, 1>{});
+    main_tile(it, I0{}, std::true_type{});
+    main_tile(it + 1, I1{}, std::true_type{});
   }
   if (it < n_full) {
-    main_tile(it, std::integral_constant<int, 0>{});
+    main_tile(it, I0{}, std::true_type{});
     ++it;
   }
   for (; it < n_tiles; ++it) {

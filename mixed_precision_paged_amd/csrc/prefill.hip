@@ -9,9 +9,10 @@
 // P.V product, accumulation is fp32.
 //
 // This is a dense QK^T / PV contraction, so it runs on the matrix cores
-// (v_mfma_f32_32x32x16_f16, gfx950).  Workgroup = 32 NW query rows of one
-// query head of one prompt; wavefront w owns rows [32w, 32w+32).  Per 32-key
-// unit each wavefront computes
+// (v_mfma_f32_32x32x16_f16, gfx950).  Workgroup = NW blocks of 32 query
+// rows of one prompt: 32 NW positions of one query head, or (head dim 128,
+// 4 wavefronts) 32 positions of up to 4 query heads that share a KV head;
+// each wavefront owns one block.  Per 32-key unit each wavefront computes
 //     S^T[key][q] = K . Q^T      (A = K from LDS, B = Q in registers)
 //     O^T[d][q]  += V^T . P^T    (A = V^T from LDS, B = P^T in registers)
 // so that with the 32x32 output layout every per-query quantity (running max,

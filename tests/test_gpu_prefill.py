@@ -212,7 +212,13 @@ def test_prefill_running_max_moving_in_most_units(lens, hq, hkv, d):
     out = torch.empty((T, hq, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((T, hq), dtype=torch.float32, device="cuda")
     ekv().ekv_prefill_attention(dev(q), dev(k), dev(v), dev(cu), dev(ks), int(max(lens)), sm, out, lse)
-    # the same rows as TARGET pages (prompt p's rows in its own pages, a permuted page order)
+    _check_both_routes(q, k, v, lens, cu, ks, hkv, d, sm, out, lse)
+
+
+def _check_both_routes(q, k, v, lens, cu, ks, hkv, d, sm, out, lse):
+    """The direct route over the same rows as TARGET pages (prompt p's rows in its own pages, a
+    permuted page order) bit-equal to the workspace route's out/lse, and sampled rows of both
+    against the oracle."""
     npg = [(L + 15) // 16 for L in lens]
     pool_k = np.zeros((sum(npg), 16, hkv, d), np.float16)
     pool_v = np.zeros_like(pool_k)
@@ -241,3 +247,23 @@ def test_prefill_running_max_moving_in_most_units(lens, hq, hkv, d):
     want, wlse = oracle.prefill_attention(q, k, v, cu, ks, True, sm, rows=sample)
     assert_close(got[sample], want[sample])
     assert_lse_close(glse[sample], wlse[sample])
+
+
+@pytest.mark.parametrize("lens,mult", [([2305, 700, 64], 3.0), ([700, 130, 33], 5.0), ([2100, 999], 5.0)])
+def test_prefill_sharp_softmax_on_normal_data(lens, mult):
+    """Softmax scale mult / sqrt(d) on N(0,1) data: each unit's scores spread over tens of log2
+    units, so a row's first units are overtaken by far larger scores again and again and the
+    redo of a unit whose weights pass 2^tau runs in many wavefronts.  Both routes against the
+    oracle, the direct route over TARGET pages bit-equal to the workspace route."""
+    step(f"prefill sharp softmax lens={lens} scale x{mult}")
+    hq, hkv, d = 32, 8, 128
+    rng = np.random.default_rng(950 + len(lens) + int(mult))
+    T = int(sum(lens))
+    q, k, v = (rng.standard_normal((T, h, d)).astype(np.float16) for h in (hq, hkv, hkv))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ks = cu[:-1].copy()
+    sm = mult / np.sqrt(d)
+    out = torch.empty((T, hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+    ekv().ekv_prefill_attention(dev(q), dev(k), dev(v), dev(cu), dev(ks), int(max(lens)), sm, out, lse)
+    _check_both_routes(q, k, v, lens, cu, ks, hkv, d, sm, out, lse)
